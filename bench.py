@@ -1,0 +1,196 @@
+#!/usr/bin/env python3
+"""Throughput of the W4A4 RPBH rotate-then-quantize linear layer on one MI355X.
+
+Workload: the image-DiT projection -- 4096 bf16 tokens, d_in = d_out = 3072,
+RPBH block h = 128, 16-level Lloyd-Max codebooks for weights and activations,
+bf16 output (synthetic inputs of that shape and distribution, see synth).
+
+One step = the whole run-time path on one batch: the fused rotate + quantize
+of the activations (orbit_quant_act) and the codebook-decode GEMM with its
+r s / K epilogue (orbit_qlinear).  The weights are packed once beforehand: in
+the method the rotation is absorbed into the weights offline.
+
+Reported: effective TFLOP/s of the layer, 2 M N K / (t_quant + t_gemm); the
+GEMM's TFLOP/s against the fp16 dense MFMA peak; the rotate/quant stage's
+GB/s against the HBM peak.  Per-kernel times come from HIP events recorded on
+the stream the kernels run on.  Activations rotate through a pool of buffers
+larger than the 256 MB Infinity Cache, so the quant stage reads from HBM.
+The oracle (fp64, host cores) is timed on the same workload as a baseline.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+PEAK_MFMA_F16 = 2516.6   # TFLOP/s, MI355X dense fp16/bf16
+PEAK_HBM = 8000.0        # GB/s, MI355X HBM3E
+POOL_BYTES = 600 << 20   # > 2x the 256 MB Infinity Cache
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", default=os.path.join(HERE, "profiles", "traffic.json"),
+                    help="per-launch HBM bytes measured with rocprofv3 counters")
+    return ap.parse_args()
+
+
+def cpu_baseline(inp, rounds_target_s=10.0):
+    """The oracle as it stands, on this host's cores: rotate + quantize the
+    activations and the fp64 product from codes, for a bounded token sample."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    X64 = oracle.bf16_bits_to_f64(inp["X"])
+    W64 = oracle.bf16_bits_to_f64(inp["W"])
+    cb = oracle.codebook(4)
+    w = oracle.pack_weights(W64, inp["perm"], inp["signs"], inp["h"], cb, 4)  # offline, untimed
+    K, N = inp["K"], inp["N"]
+
+    def run(rows):
+        a = oracle.quant_act(X64[:rows], inp["perm"], inp["signs"], inp["h"], cb, 4, inp["eps"])
+        oracle.qlinear_codes(a["idx"], a["s"], cb["centroids"], w["idx"], w["r_bf16"],
+                             cb["centroids"], K)
+
+    run(64)  # warm-up
+    rows, elapsed, total_rows = 512, 0.0, 0
+    t0 = time.perf_counter()
+    while elapsed < rounds_target_s and total_rows < 4 * inp["M"]:
+        run(rows)
+        total_rows += rows
+        elapsed = time.perf_counter() - t0
+    flops = 2.0 * total_rows * N * K
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{total_rows} tokens of the 4096-token workload in blocks of {rows} "
+                      f"(rotate + quantize + fp64 product from codes), {elapsed:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path is not "
+              "sharded across GPUs in this build", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import rotation_bit_ptq_amd as rbp
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = synth.make(2)
+    M, K, N, h = inp["M"], inp["K"], inp["N"], inp["h"]
+
+    rot = rbp.Rotation(inp["perm"], inp["signs"], h, dev)
+    cb = rbp.Codebook(K, 4)
+    x_bytes = M * K * 2
+    pool_n = max(2, POOL_BYTES // x_bytes)
+    X0 = torch.from_numpy(inp["X"].view(np.int16)).view(torch.bfloat16).to(dev)
+    pool = [X0] + [X0.clone() for _ in range(pool_n - 1)]
+    W = torch.from_numpy(inp["W"].view(np.int16)).view(torch.bfloat16).to(dev)
+    iw, r = rbp.pack_weights(rot, cb, W)           # offline
+
+    idx_a = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    s = torch.empty((M,), dtype=torch.float32, device=dev)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+    import ctypes
+    lib = rbp.lib
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def quant(X):
+        st = lib.orbit_quant_act(ctypes.byref(rot.struct), ctypes.byref(cb.struct),
+                                 ctypes.c_void_p(X.data_ptr()), 1, M, K, inp["eps"],
+                                 ctypes.c_void_p(idx_a.data_ptr()), ctypes.c_void_p(s.data_ptr()),
+                                 None, sp)
+        assert st == 0, st
+
+    def gemm():
+        st = lib.orbit_qlinear(ctypes.c_void_p(idx_a.data_ptr()), ctypes.c_void_p(s.data_ptr()),
+                               ctypes.byref(cb.struct), ctypes.c_void_p(iw.data_ptr()),
+                               ctypes.c_void_p(r.data_ptr()), ctypes.byref(cb.struct), None, 0,
+                               M, N, K, ctypes.c_void_p(out.data_ptr()), 1, sp)
+        assert st == 0, st
+
+    for i in range(args.warmup):
+        quant(pool[i % pool_n])
+        gemm()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        e = ev[i]
+        e[0].record(stream)
+        quant(pool[i % pool_n])
+        e[1].record(stream)
+        gemm()
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    tq = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3
+    tg = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
+    ms_per_step = wall / args.steps * 1e3
+    flops = 2.0 * M * N * K
+    quant_bytes = M * K * 2 + M * K // 2 + M * 4      # bf16 in, 4-bit codes + fp32 s out
+    gemm_tflops = flops / tg.mean() / 1e12
+    quant_gbps = quant_bytes / tq.mean() / 1e9
+    value = flops / (wall / args.steps) / 1e12
+
+    traffic = None
+    if os.path.exists(args.traffic):
+        try:
+            traffic = json.load(open(args.traffic)).get("qlinear_gemm_bytes")
+        except Exception:  # noqa: BLE001
+            traffic = None
+
+    line = {
+        "metric": "W4A4 RPBH qlinear effective TFLOP/s + rotate/quant stage HBM GB/s",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "image-DiT projection W4A4: 4096 bf16 tokens x d_in 3072 -> "
+                               "d_out 3072, RPBH h=128, 16-level act/weight codebooks, bf16 out",
+                   "tokens": M, "d_in": K, "d_out": N, "h": h, "bits_a": 4, "bits_w": 4},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_MFMA_F16,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_MFMA_F16, 4),
+                     "traffic": traffic, "kernel": "orbit_qlinear (codebook-decode GEMM)"},
+        "roofline_quant": {"bound": "hbm", "achieved": round(quant_gbps, 1), "peak": PEAK_HBM,
+                           "unit": "GB/s", "frac": round(quant_gbps / PEAK_HBM, 4),
+                           "kernel": "orbit_quant_act (fused rotate + quantize)",
+                           "bytes_per_launch": quant_bytes},
+        "gemm_us": round(tg.mean() * 1e6, 2),
+        "quant_us": round(tq.mean() * 1e6, 2),
+        "quant_gbps": round(quant_gbps, 1),
+        "gemm_tflops": round(gemm_tflops, 2),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,181 @@
+/*
+ * orbit.h -- C ABI of the rotate-then-quantize linear layer for AMD MI355X
+ * (gfx950).  Library: liborbit.so (rotation_bit_ptq_amd/liborbit.so).
+ *
+ * The method (OrbitQuant paper page on hyper.ai, section Method):
+ *   offline  W' = W Pi_d^T; row norms r'_i = ||w'_i|| stored in BF16; unit
+ *            rows quantized by one Lloyd-Max codebook C_d.
+ *   online   x' = Pi_d x; s = ||x'||; x' / (s + eps) quantized by C_d.
+ *   product  out[m, n] = r_n s_m <Q(w~_n), Q(x~_m)>  ~  (W x_m)_n,
+ *            with no inverse rotation at run time.
+ *   Pi_d = blkdiag(H_h D_1, ..., H_h D_{d/h}) P_pi  (the RPBH rotation).
+ * And the int8 rotated weight-only path of the int8 article (cloud.baidu.com,
+ * "量化旋转压缩主模型技术解析", section 4): rotate, per-group scale, round;
+ * at run time dequantize and undo the rotation (computed here in the equal
+ * form (X Pi^T) (W^')^T, so the weights are never inverse-rotated).
+ *
+ * Conventions shared by every entry point
+ *   - Readings of the pages: (P_pi x)_k = x[perm[k]] (gather); sign bit k
+ *     applies to permuted coordinate k; H_h is Sylvester-ordered and scaled
+ *     by 1/sqrt(h), so Pi_d is orthogonal.
+ *   - Codebooks are in N(0,1) units: coordinate v of a unit vector in
+ *     dimension d is coded as idx = #{j : thresholds[j] < sqrt(d) * v} and
+ *     decodes to centroids[idx] / sqrt(d).  The decision is taken in float32.
+ *   - Packed indices: row-major, one LSB-first bit stream per row; index k
+ *     takes bits [k*bits, (k+1)*bits); a row of d indices is d*bits/8 bytes.
+ *   - Ownership: the caller owns every buffer.  Pointers named "device" are
+ *     HIP device memory; structs passed by pointer are host memory read only
+ *     during the call.  The library allocates no device memory and keeps no
+ *     state between calls; every entry point is thread-safe.
+ *   - Asynchrony: device work is enqueued on `stream` (0 = the default
+ *     stream) and the call returns without synchronizing.  Buffers must not
+ *     alias.
+ *   - Errors: no entry point throws or aborts.  Arguments are validated on
+ *     the host before any HIP call; a bad argument returns ORBIT_E_ARG
+ *     (null pointer, bad enum, unsorted codebook), ORBIT_E_SHAPE (sizes) or
+ *     ORBIT_E_DTYPE, with nothing enqueued.  A failed launch returns
+ *     ORBIT_E_HIP and orbit_last_hip_error() gives the HIP code.
+ */
+#ifndef ORBIT_H
+#define ORBIT_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ORBIT_OK = 0,
+  ORBIT_E_ARG = 1,
+  ORBIT_E_SHAPE = 2,
+  ORBIT_E_DTYPE = 3,
+  ORBIT_E_UNSUPPORTED = 4,
+  ORBIT_E_HIP = 5
+} orbit_status;
+
+typedef enum { ORBIT_F32 = 0, ORBIT_BF16 = 1, ORBIT_F16 = 2 } orbit_dtype;
+
+/* RPBH rotation parameters (the int8 article's "rotation metadata").
+ * d: dimension, a multiple of h, 16 <= d <= ORBIT_MAX_D.
+ * h: Hadamard block size, a power of two, 16 <= h <= 1024.
+ * perm: device int32[d], a permutation of 0..d-1 (gather order).
+ * sign_bits: device uint32[(d + 31) / 32]; bit k%32 of word k/32 set means
+ *            D_k = -1 for permuted coordinate k.
+ * Variants of the rotation ablation (OrbitQuant page, Experiments): an
+ * identity perm gives Block-RHT, h = d gives the full RHT (d a power of two
+ * up to 1024). */
+typedef struct {
+  int32_t d;
+  int32_t h;
+  const int32_t *perm;
+  const uint32_t *sign_bits;
+} orbit_rpbh;
+
+#define ORBIT_MAX_D 16384
+#define ORBIT_MAX_LEVELS 256
+
+/* Lloyd-Max codebook in N(0,1) units (OrbitQuant page, Method: one
+ * codebook per input dimension d, fitted offline to the fixed marginal
+ * f_d ~ N(0, 1/d); by scale equivariance that is the N(0,1) codebook divided
+ * by sqrt(d)).  Levels = 2^bits.  centroids ascending and symmetric;
+ * thresholds[j] = (centroids[j] + centroids[j+1]) / 2, the middle one 0. */
+typedef struct {
+  int32_t bits; /* 1, 2, 3, 4, 6 or 8 */
+  int32_t d;    /* dimension it serves (informational; the table is d-free) */
+  float centroids[ORBIT_MAX_LEVELS];
+  float thresholds[ORBIT_MAX_LEVELS - 1];
+} orbit_codebook;
+
+/* Text of a status code (static storage). */
+const char *orbit_status_string(orbit_status status);
+
+/* The last HIP error code seen by a failed call on this thread (0 if none). */
+int orbit_last_hip_error(void);
+
+/* Fit the Lloyd-Max codebook for N(0,1) with 2^bits levels, in fp64, on the
+ * host (OrbitQuant page, Method: Lloyd-Max run offline on the marginal).
+ * Alternates the nearest-neighbour and centroid conditions, then polishes
+ * with Newton steps on the thresholds until the step is below `tol`
+ * (<= 0 selects 1e-15) or `max_iter` Newton steps (<= 0 selects 100).
+ * out: receives the float32 tables (required).  centroids_f64[2^bits],
+ * thresholds_f64[2^bits - 1] and mse_f64 (the distortion E[(X - Q(X))^2])
+ * are optional host outputs (may be NULL).  No device work.
+ * Errors: ORBIT_E_ARG (bits not in {1,2,3,4,6,8}, out NULL, d < 1). */
+orbit_status orbit_fit_codebook(int32_t d, int32_t bits, int32_t max_iter, double tol,
+                                orbit_codebook *out, double *centroids_f64,
+                                double *thresholds_f64, double *mse_f64);
+
+/* Offline weight packer (OrbitQuant page, Method, offline stage):
+ * W' = W Pi^T row by row, r_n = ||w'_n|| rounded to bf16 (nearest even),
+ * u = sqrt(d) w'_n / r_n (u = 0 for a zero row), idx = #{t_j < u}.
+ * W: device [d_out, d_in] row-major, w_dtype F32 or BF16; rot->d == d_in.
+ * idx_out: device uint8 [d_out, d_in * cw->bits / 8]; r_bf16_out: device
+ * uint16 [d_out] (bf16 bits).  d_out >= 0 (0 enqueues nothing). */
+orbit_status orbit_pack_weights(const orbit_rpbh *rot, const orbit_codebook *cw,
+                                const void *W, orbit_dtype w_dtype,
+                                int64_t d_out, int64_t d_in,
+                                uint8_t *idx_out, uint16_t *r_bf16_out,
+                                hipStream_t stream);
+
+/* Online activation rotate + quantize (OrbitQuant page, Method, inference):
+ * x' = Pi x, s = ||x'|| (fp32), u = sqrt(d) x' / (s + eps), idx = #{t_j < u}.
+ * X: device [M, d] row-major, F32 or BF16.  idx_out: device uint8
+ * [M, d * ca->bits / 8]; s_out: device float [M]; xrot_f32_debug: optional
+ * device float [M, d] receiving x' (NULL to skip).  eps >= 0. */
+orbit_status orbit_quant_act(const orbit_rpbh *rot, const orbit_codebook *ca,
+                             const void *X, orbit_dtype x_dtype, int64_t M, int64_t d,
+                             float eps, uint8_t *idx_out, float *s_out,
+                             float *xrot_f32_debug, hipStream_t stream);
+
+/* Codebook-decode GEMM (OrbitQuant page, Method: W^' x^' with the rotation
+ * cancelled):  out[m, n] = s[m] * r[n] / K * sum_k ca[ia[m,k]] * cw[iw[n,k]]
+ *              (+ bias[n]).
+ * idx_a: device [M, K*ca->bits/8]; s: device float [M]; idx_w: device
+ * [N, K*cw->bits/8]; r_bf16: device uint16 [N]; bias: optional device [N]
+ * (F32 or BF16, bias_dtype ignored when NULL); out: device [M, N], F32 or
+ * BF16 (nearest even).  The products run on fp16 matrix cores with float32
+ * accumulation.  Bits: ca 2/3/4/6/8, cw 2/3/4/6/8.  K % 128 == 0,
+ * 128 <= K <= 65536; M, N >= 0. */
+orbit_status orbit_qlinear(const uint8_t *idx_a, const float *s, const orbit_codebook *ca,
+                           const uint8_t *idx_w, const uint16_t *r_bf16,
+                           const orbit_codebook *cw, const void *bias, orbit_dtype bias_dtype,
+                           int64_t M, int64_t N, int64_t K, void *out, orbit_dtype out_dtype,
+                           hipStream_t stream);
+
+/* Rotation alone: out = Pi x per row (the int8 path's run-time step, and a
+ * debugging aid).  X: device [M, d] F32 or BF16; out: device [M, d],
+ * out_dtype F32 or F16 (nearest even). */
+orbit_status orbit_rotate(const orbit_rpbh *rot, const void *X, orbit_dtype x_dtype,
+                          int64_t M, int64_t d, void *out, orbit_dtype out_dtype,
+                          hipStream_t stream);
+
+/* Int8 rotated weight packer (int8 article, section 4 pack_weight):
+ * W' = W Pi^T; for each row and each group of `group` consecutive columns
+ * scale = fp16(max|w'| / 127) (float32 division, nearest even);
+ * q = clamp(round_half_even(w' / scale), -127, 127), q = 0 where scale = 0.
+ * W: device [N, K] F32 or BF16; q_out: device int8 [N, K];
+ * scale_f16_out: device uint16 [N, K/group] (fp16 bits).
+ * group a multiple of 16 dividing K, group <= 1024. */
+orbit_status orbit_int8_pack_weights(const orbit_rpbh *rot, const void *W, orbit_dtype w_dtype,
+                                     int64_t N, int64_t K, int32_t group,
+                                     int8_t *q_out, uint16_t *scale_f16_out,
+                                     hipStream_t stream);
+
+/* Int8 weight-only GEMM on rotated activations (int8 article, section 4
+ * load_and_run, in the equal form that needs no inverse rotation):
+ * out[m, n] = sum_k Xrot[m,k] * q[n,k] * scale[n, k/group]  (+ bias[n]).
+ * Xrot: device [M, K] F16 (from orbit_rotate); q: device int8 [N, K];
+ * scale_f16: device uint16 [N, K/group]; group == 128; K % 128 == 0;
+ * out: device [M, N], F32 or BF16.  Weights are decoded to fp16 (q times
+ * scale, one rounding) and multiplied on fp16 matrix cores, fp32 accumulate. */
+orbit_status orbit_int8_linear(const void *Xrot, orbit_dtype xrot_dtype, int64_t M, int64_t K,
+                               const int8_t *q, const uint16_t *scale_f16, int32_t group,
+                               int64_t N, const void *bias, orbit_dtype bias_dtype,
+                               void *out, orbit_dtype out_dtype, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ORBIT_H */

@@ -1,0 +1,95 @@
+// Internal declarations shared by the host ABI layer and the kernel files.
+#pragma once
+
+#include <stdint.h>
+
+#include <atomic>
+
+#include "../../include/orbit.h"
+
+namespace orbit {
+
+// Per-device properties queried once (LDS per block, compute units).
+struct DeviceInfo {
+  int max_lds = 0;
+  int n_cu = 0;
+};
+hipError_t device_info(DeviceInfo* out);
+
+// One launch site's cached setup: the dynamic-LDS limit raised once per
+// device, and the occupancy for the last LDS size asked about.
+struct LaunchCache {
+  std::atomic<unsigned long long> lds_raised{0};  // bit per device
+  std::atomic<long long> occ_key{-1};             // (device << 32) | lds
+  std::atomic<int> occ_blocks{0};
+};
+hipError_t prepare_launch(LaunchCache& c, const void* kern, int threads, int lds, int* blocks_per_cu);
+
+// ---- rotate + quantize family (rpbh_quant.hip) ----------------------------
+
+enum class RowMode : int {
+  kActQuant = 0,     // s = ||x'||, u = sqrt(d) x' / (s + eps)
+  kWeightQuant = 1,  // r = ||w'|| (bf16), u = sqrt(d) w' / r
+  kRotate = 2,       // x' only
+  kInt8Pack = 3,     // per-group fp16 scale, int8 codes
+};
+
+// Uniform-grid lookup that turns "count thresholds below u" into one table
+// read and one compare (see rpbh_quant.hip).  Chosen on the host.
+struct GridSearch {
+  float a, b;   // cell = clamp(floor(fma(u, a, b)), 0, cells - 1)
+  int cells;    // power of two <= kMaxGridCells
+  int nthr;     // number of thresholds (levels - 1)
+};
+constexpr int kMaxGridCells = 2048;
+
+struct RowJob {
+  RowMode mode;
+  int in_dtype;    // orbit_dtype of the rows
+  int out_dtype;   // kRotate: F32 / F16
+  int64_t rows;
+  int d, h;
+  const int32_t* perm;
+  const uint32_t* sign_bits;
+  const void* in;
+  // quantize outputs
+  int bits;
+  const float* thresholds;  // host pointer (levels - 1 floats)
+  GridSearch grid;
+  float eps;
+  uint8_t* idx_out;
+  float* norm_f32_out;      // act: s
+  uint16_t* norm_bf16_out;  // weight: r
+  float* xrot_f32_out;      // debug / rotate F32 output
+  void* rot_out;            // rotate F16 output
+  // int8 outputs
+  int group;
+  int8_t* q_out;
+  uint16_t* scale_out;
+};
+
+hipError_t launch_rows(const RowJob& job, hipStream_t stream);
+
+// ---- decode GEMMs (qgemm.hip) ----------------------------------------------
+
+struct GemmJob {
+  int kind;  // 0: codebook x codebook, 1: fp16 x int8
+  int64_t M, N, K;
+  const uint8_t* a;        // kind 0: idx_a; kind 1: fp16 Xrot
+  const uint8_t* b;        // kind 0: idx_w; kind 1: int8 q
+  int bits_a, bits_b;      // kind 0
+  const float* cent_a;     // host, 2^bits_a
+  const float* cent_b;     // host, 2^bits_b
+  const float* s;          // kind 0: per-row scale of A (device)
+  const uint16_t* r_bf16;  // kind 0: per-row scale of B (device, bf16)
+  const uint16_t* scale_f16;  // kind 1: group scales (device)
+  int group;
+  const void* bias;
+  int bias_dtype;
+  void* out;
+  int out_dtype;
+};
+
+hipError_t launch_gemm(const GemmJob& job, hipStream_t stream);
+
+}  // namespace orbit

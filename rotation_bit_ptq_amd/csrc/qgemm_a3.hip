@@ -1,0 +1,8 @@
+// Decode-GEMM kernels for 3-bit activation codes (see qgemm_impl.h).
+#include "qgemm_impl.h"
+
+namespace orbit {
+namespace qgemm {
+ORBIT_DEFINE_LAUNCH_CODES_B(3)
+}  // namespace qgemm
+}  // namespace orbit

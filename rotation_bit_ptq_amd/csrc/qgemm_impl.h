@@ -1,0 +1,596 @@
+#pragma once
+// Decode GEMMs on fp16 matrix cores (gfx950 v_mfma_f32_32x32x16_f16).
+//
+// OrbitQuant page, Method: because W' = W Pi^T and x' = Pi x, the layer is
+// the product of the two quantized factors with no inverse rotation:
+//   out[m, n] = s_m r_n (1/K) sum_k ca[ia[m,k]] cw[iw[n,k]]
+// (codebooks in N(0,1) units).  The int8 article's load-and-run (section 4)
+// is computed in the equal form out = (X Pi^T) (q * scale)^T.
+//
+// Work layout:
+//   * one workgroup = 4 waves = one output tile of TM tokens x TN weight
+//     rows; the waves form a 2 x 2 grid, each computing (TM/2) x (TN/2) as
+//     WM x WN blocks of 32 x 32 (one wave per SIMD: the 32x32x16 MFMA keeps
+//     the matrix core busy from a single wave, the 16x16x32 one does not);
+//   * MFMA "A" operand = weight rows (n), "B" operand = tokens (m): lane l
+//     feeds row / column l % 32 and holds outputs n = 8 (q/4) + 4 (l/32) +
+//     q%4 (q < 16) of token l % 32, i.e. four runs of four consecutive n;
+//   * the K loop runs in chunks of KC = 16 * STEPS; within a chunk, lane
+//     half g = l / 32 of both operands owns the contiguous k range
+//     [g KC/2, (g+1) KC/2), and sub-step s feeds k = g KC/2 + 8 s + 0..7.
+//     Both operands use the same assignment, so every dot product is the
+//     exact sum over all k while each lane reads one contiguous run of
+//     packed codes per row per chunk (32 bytes for 4-bit codes);
+//   * codes go straight from global memory to registers (the next chunk is
+//     in flight while the current one is multiplied) and are decoded with
+//     an LDS table replicated per lane: a code byte and the lane number form
+//     the table address in one v_perm, every lane hits its own bank, and a
+//     4-bit byte yields two fp16 values per read (a 2-bit byte four);
+//   * codebook values are fp16 in N(0,1) units, products accumulate in
+//     fp32; s_m r_n / K (+ bias) is applied once in fp32 in the epilogue and
+//     the result is rounded once (bf16 nearest even, or kept in fp32).
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+
+#include "orbit_internal.h"
+
+namespace orbit {
+namespace qgemm {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+struct GemmArgs {
+  long long M, N, K;
+  const uint8_t* a;   // token operand (codes, or fp16 rows for the int8 GEMM)
+  const uint8_t* b;   // weight operand (codes, or int8 rows)
+  long long lda, ldb; // bytes per row
+  const float* s;
+  const uint16_t* r_bf16;
+  const uint16_t* scale_f16;
+  int groups_per_row;
+  float inv_k;
+  const void* bias;
+  int bias_dtype;
+  void* out;
+  int out_dtype;
+  int tiles_m, tiles_n;
+  int table_a_offset;  // LDS byte offset of the activation codebook table
+  int table_b_offset;  // LDS byte offset of the weight codebook table
+  uint16_t cent_a[256];
+  uint16_t cent_b[256];
+};
+
+// Loads from an absolute LDS byte address (the decode tables start at LDS
+// offset 0; the kernels use no static LDS).
+typedef __attribute__((address_space(3))) const uint32_t lds_u32_t;
+typedef __attribute__((address_space(3))) const uint16_t lds_u16_t;
+typedef __attribute__((address_space(3))) const u32x2 lds_u32x2_t;
+__device__ __forceinline__ uint32_t lds_u32(uint32_t a) { return *(lds_u32_t*)(uintptr_t)a; }
+__device__ __forceinline__ uint32_t lds_u16(uint32_t a) { return *(lds_u16_t*)(uintptr_t)a; }
+__device__ __forceinline__ u32x2 lds_u32x2(uint32_t a) { return *(lds_u32x2_t*)(uintptr_t)a; }
+
+// ---------------------------------------------------------------- operands
+// Each operand type knows its chunk (kChunkK), how many bytes a lane loads
+// per chunk for one 32-row block, and how to turn sub-step s into a half8.
+
+template <int BITS>
+struct CodeOp {  // packed b-bit codebook indices, LSB-first
+  static constexpr int kBits = BITS;
+  static constexpr int kChunkK = 128;                 // 8 sub-steps of k = 16
+  static constexpr int kBytes = 8 * BITS;              // 64 codes per lane per chunk
+  static constexpr int kDwords = kBytes / 4;
+  static constexpr int kTableBytes = (BITS == 4 || BITS == 2 || BITS == 8) ? 65536 : 16384;
+  uint32_t w[kDwords];
+
+  __device__ __forceinline__ void load(const uint8_t* p) {
+    if constexpr (kBytes % 16 == 0) {
+#pragma unroll
+      for (int q = 0; q < kBytes / 16; ++q) {
+        const u32x4 v = *(const u32x4*)(p + 16 * q);
+        w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
+      }
+    } else {
+      static_assert(kBytes % 8 == 0, "unsupported width");
+#pragma unroll
+      for (int q = 0; q < kBytes / 8; ++q) {
+        const u32x2 v = *(const u32x2*)(p + 8 * q);
+        w[2 * q] = v.x; w[2 * q + 1] = v.y;
+      }
+    }
+  }
+
+  // bits [lo, lo + n) of the lane's code stream (n <= 32)
+  __device__ __forceinline__ uint32_t field(int lo, int n) const {
+    const int wi = lo >> 5, sh = lo & 31;
+    uint32_t v = (sh + n <= 32) ? (w[wi] >> sh) : __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh);
+    return n == 32 ? v : (v & ((1u << n) - 1u));
+  }
+
+  // `lb` is the lane's base in the decode table (see lane_base); every
+  // table address is formed in one v_perm or v_lshl_or and read straight
+  // from LDS.
+  __device__ __forceinline__ half8 decode(int s, uint32_t lb) const {
+    uint32_t o[4];
+    if constexpr (BITS == 4) {
+      // table [byte][64 lanes] of fp16 pairs: addr = base | byte << 8 | lane << 2
+      const uint32_t x = w[s];
+      o[0] = lds_u32(__builtin_amdgcn_perm(x, lb, 0x0c020400u));
+      o[1] = lds_u32(__builtin_amdgcn_perm(x, lb, 0x0c020500u));
+      o[2] = lds_u32(__builtin_amdgcn_perm(x, lb, 0x0c020600u));
+      o[3] = lds_u32(__builtin_amdgcn_perm(x, lb, 0x0c020700u));
+    } else if constexpr (BITS == 2) {
+      // table [byte][32 lanes] of fp16 quads: addr = base | byte << 8 | (lane & 31) << 3
+      const uint32_t x = w[s >> 1];
+      const uint32_t sel0 = (s & 1) ? 0x0c020600u : 0x0c020400u;
+      const uint32_t sel1 = (s & 1) ? 0x0c020700u : 0x0c020500u;
+      const u32x2 q0 = lds_u32x2(__builtin_amdgcn_perm(x, lb, sel0));
+      const u32x2 q1 = lds_u32x2(__builtin_amdgcn_perm(x, lb, sel1));
+      o[0] = q0.x; o[1] = q0.y; o[2] = q1.x; o[3] = q1.y;
+    } else if constexpr (BITS == 8) {
+      // table [byte][64 lanes], fp16 in the low half of each entry
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t x = w[2 * s + (j >> 1)];
+        const uint32_t s0 = (j & 1) ? 0x0c020600u : 0x0c020400u;
+        const uint32_t s1 = (j & 1) ? 0x0c020700u : 0x0c020500u;
+        o[j] = lds_u16(__builtin_amdgcn_perm(x, lb, s0)) | (lds_u16(__builtin_amdgcn_perm(x, lb, s1)) << 16);
+      }
+    } else if constexpr (BITS == 6) {
+      // table [index][64 lanes], fp16 in the low half of each entry
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t i0 = field(48 * s + 12 * j, 6), i1 = field(48 * s + 12 * j + 6, 6);
+        o[j] = lds_u16((i0 << 8) | lb) | (lds_u16((i1 << 8) | lb) << 16);
+      }
+    } else {
+      static_assert(BITS == 3, "unsupported width");
+      // table [pair of 3-bit indices][64 lanes] of fp16 pairs
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = lds_u32((field(24 * s + 6 * j, 6) << 8) | lb);
+    }
+    return __builtin_bit_cast(half8, make_uint4(o[0], o[1], o[2], o[3]));
+  }
+
+  // The lane's table base: the table's LDS offset (a multiple of 64 KB for
+  // the v_perm-addressed tables, of 16 KB for the others) plus the lane's
+  // column inside each entry row.
+  static __device__ __forceinline__ uint32_t lane_base(uint32_t table_off, uint32_t lane) {
+    return table_off | (BITS == 2 ? ((lane & 31u) << 3) : (lane << 2));
+  }
+};
+
+// Builds the lane-replicated decode table of a codebook in LDS.
+template <int BITS>
+__device__ void build_table(char* tab, const uint16_t* cent) {
+  if constexpr (BITS == 4) {
+    for (int e = threadIdx.x; e < 256 * 64; e += blockDim.x) {
+      const int byte = e >> 6;
+      ((uint32_t*)tab)[e] = (uint32_t)cent[byte & 15] | ((uint32_t)cent[byte >> 4] << 16);
+    }
+  } else if constexpr (BITS == 2) {
+    for (int e = threadIdx.x; e < 256 * 32; e += blockDim.x) {
+      const int byte = e >> 5;
+      uint2 q;
+      q.x = (uint32_t)cent[byte & 3] | ((uint32_t)cent[(byte >> 2) & 3] << 16);
+      q.y = (uint32_t)cent[(byte >> 4) & 3] | ((uint32_t)cent[byte >> 6] << 16);
+      ((uint2*)tab)[e] = q;
+    }
+  } else if constexpr (BITS == 8) {
+    for (int e = threadIdx.x; e < 256 * 64; e += blockDim.x) ((uint32_t*)tab)[e] = cent[e >> 6];
+  } else if constexpr (BITS == 6) {
+    for (int e = threadIdx.x; e < 64 * 64; e += blockDim.x) ((uint32_t*)tab)[e] = cent[e >> 6];
+  } else {
+    for (int e = threadIdx.x; e < 64 * 64; e += blockDim.x) {
+      const int pair = e >> 6;
+      ((uint32_t*)tab)[e] = (uint32_t)cent[pair & 7] | ((uint32_t)cent[pair >> 3] << 16);
+    }
+  }
+}
+
+struct F16Op {  // fp16 rows (rotated activations of the int8 GEMM)
+  static constexpr int kChunkK = 32;  // 2 sub-steps
+  static constexpr int kBytes = 32;   // 16 halves per lane per chunk
+  u32x4 v[2];
+  __device__ __forceinline__ void load(const uint8_t* p) {
+    v[0] = *(const u32x4*)p;
+    v[1] = *(const u32x4*)(p + 16);
+  }
+  __device__ __forceinline__ half8 decode(int s, uint32_t) const {
+    return __builtin_bit_cast(half8, v[s]);
+  }
+  static __device__ __forceinline__ uint32_t lane_base(uint32_t, uint32_t) { return 0; }
+};
+
+struct I8Op {  // int8 weight rows with an fp16 scale for the chunk's group
+  static constexpr int kChunkK = 32;
+  static constexpr int kBytes = 16;  // 16 codes per lane per chunk
+  u32x4 v;
+  uint32_t scale2;  // the group's fp16 scale in both halves
+  __device__ __forceinline__ void load(const uint8_t* p) { v = *(const u32x4*)p; }
+  static __device__ __forceinline__ uint32_t lane_base(uint32_t, uint32_t) { return 0; }
+  __device__ __forceinline__ half8 decode(int s, uint32_t) const {
+    // q + 128 as an unsigned byte u; fp16 bits 0x6400 | u = 1024 + u exactly;
+    // subtracting 1152 gives q exactly; one multiply by the scale rounds once
+    const uint32_t w0 = (s ? v.z : v.x) ^ 0x80808080u;
+    const uint32_t w1 = (s ? v.w : v.y) ^ 0x80808080u;
+    const uint32_t mag = 0x64646464u;
+    uint32_t h[4];
+    h[0] = __builtin_amdgcn_perm(mag, w0, 0x04010400u);
+    h[1] = __builtin_amdgcn_perm(mag, w0, 0x04030402u);
+    h[2] = __builtin_amdgcn_perm(mag, w1, 0x04010400u);
+    h[3] = __builtin_amdgcn_perm(mag, w1, 0x04030402u);
+    typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+    const half2v bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+    const half2v sc = __builtin_bit_cast(half2v, scale2);
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      half2v q = __builtin_bit_cast(half2v, h[i]) - bias;
+      o[i] = __builtin_bit_cast(uint32_t, q * sc);
+    }
+    return __builtin_bit_cast(half8, make_uint4(o[0], o[1], o[2], o[3]));
+  }
+};
+
+// two floats to packed bf16, round to nearest even (v_cvt_pk_bf16_f32);
+// NaN stays NaN
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) { return (uint16_t)pack_bf16x2(f, 0.0f); }
+
+__device__ __forceinline__ float load_bias(const GemmArgs& g, long long n) {
+  if (!g.bias) return 0.0f;
+  if (g.bias_dtype == ORBIT_BF16) return __uint_as_float((uint32_t)((const uint16_t*)g.bias)[n] << 16);
+  return ((const float*)g.bias)[n];
+}
+
+// Tile order: consecutive workgroups land on different XCDs (round robin), so
+// block b is renumbered to give each XCD a contiguous run of tiles, and runs
+// are walked in groups of kGroupM token tiles so an XCD shares its operands.
+__device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
+  constexpr int kXcd = 8, kGroupM = 4;
+  const int total = tiles_m * tiles_n;
+  const int full = (total / kXcd) * kXcd;
+  int t = b;
+  if (b < full) t = (b % kXcd) * (full / kXcd) + b / kXcd;
+  const int per_group = kGroupM * tiles_n;
+  const int grp = t / per_group;
+  const int first_m = grp * kGroupM;
+  const int gsize = min(kGroupM, tiles_m - first_m);
+  const int r = t % per_group;
+  tm = first_m + r % gsize;
+  tn = r / gsize;
+}
+
+// KIND 0: codebook x codebook; KIND 1: fp16 x int8 with group scales.
+// WM token blocks and WN weight blocks of 32 per wave.
+template <int KIND, class OpA, class OpB, int WM, int WN>
+__global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
+  extern __shared__ __align__(16) char smem[];
+  static_assert(OpA::kChunkK == OpB::kChunkK, "operands must share the chunk");
+  constexpr int KC = OpA::kChunkK;
+  constexpr int STEPS = KC / 16;
+  constexpr int TM = 64 * WM, TN = 64 * WN;
+  const uint32_t lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+
+  if constexpr (KIND == 0) {
+    build_table<OpA::kBits>(smem + g.table_a_offset, g.cent_a);
+    if (g.table_a_offset != g.table_b_offset) build_table<OpB::kBits>(smem + g.table_b_offset, g.cent_b);
+    __syncthreads();
+  }
+  const uint32_t lb_a = OpA::lane_base((uint32_t)g.table_a_offset, lane);
+  const uint32_t lb_b = OpB::lane_base((uint32_t)g.table_b_offset, lane);
+
+  int tm, tn;
+  tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
+  const long long m_base = (long long)tm * TM + wm * (TM / 2);
+  const long long n_base = (long long)tn * TN + wn * (TN / 2);
+  const int r32 = lane & 31, half = lane >> 5;
+
+  // row offsets (rows past the end are clamped; their results are dropped);
+  // 32-bit offsets from the operand base keep the loads on one scalar base
+  uint32_t oa[WM], ob[WN];
+#pragma unroll
+  for (int i = 0; i < WM; ++i) {
+    long long m = m_base + 32 * i + r32;
+    m = m < g.M ? m : g.M - 1;
+    oa[i] = (uint32_t)(m * g.lda) + (uint32_t)(half * OpA::kBytes);
+  }
+  uint32_t nrow[WN];
+#pragma unroll
+  for (int j = 0; j < WN; ++j) {
+    long long n = n_base + 32 * j + r32;
+    n = n < g.N ? n : g.N - 1;
+    nrow[j] = (uint32_t)n;
+    ob[j] = (uint32_t)(n * g.ldb) + (uint32_t)(half * OpB::kBytes);
+  }
+  constexpr uint32_t kChunkA = 2u * OpA::kBytes, kChunkB = 2u * OpB::kBytes;
+
+  floatx16 acc[WN][WM];
+#pragma unroll
+  for (int j = 0; j < WN; ++j)
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[j][i][q] = 0.0f;
+
+  // Raw codes of chunk c + 1 load into the other of two buffers while chunk
+  // c is decoded and multiplied.  Decoded token operands are single-
+  // buffered: block i is re-decoded for the next sub-step right after its
+  // last MFMA of this one; decoded weight operands alternate between two
+  // sets, the next set decoded at the start of a sub-step.
+  OpA ra0[WM], ra1[WM];
+  OpB rb0[WN], rb1[WN];
+  auto load_chunk = [&](int c, OpA (&xa)[WM], OpB (&xb)[WN]) {
+#pragma unroll
+    for (int i = 0; i < WM; ++i) xa[i].load(g.a + oa[i] + (uint32_t)c * kChunkA);
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+      xb[j].load(g.b + ob[j] + (uint32_t)c * kChunkB);
+      if constexpr (KIND == 1) {
+        const uint32_t gi = (uint32_t)(c * KC) / 128u;  // group of 128 k
+        const uint32_t sc = g.scale_f16[nrow[j] * (uint32_t)g.groups_per_row + gi];
+        xb[j].scale2 = sc | (sc << 16);
+      }
+    }
+  };
+  half8 av[WM], bv0[WN], bv1[WN];
+  auto mfmas = [&](const half8 (&bcur)[WN], int i) {
+#pragma unroll
+    for (int j = 0; j < WN; ++j)
+      acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bcur[j], av[i], acc[j][i], 0, 0, 0);
+  };
+  // MFMAs of one sub-step with operands (bcur, av) while the next sub-step
+  // (xa, xb, ns) is decoded into (av, bnext)
+  auto substep_next = [&](const OpA (&xa)[WM], const OpB (&xb)[WN], int ns,
+                          const half8 (&bcur)[WN], half8 (&bnext)[WN]) {
+#pragma unroll
+    for (int j = 0; j < WN; ++j) bnext[j] = xb[j].decode(ns, lb_b);
+#pragma unroll
+    for (int i = 0; i < WM; ++i) {
+      mfmas(bcur, i);
+      av[i] = xa[i].decode(ns, lb_a);
+    }
+    // keep the scheduler from hoisting later sub-steps' decodes (and their
+    // registers) across this point
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto substep_last = [&](const half8 (&bcur)[WN]) {
+#pragma unroll
+    for (int i = 0; i < WM; ++i) mfmas(bcur, i);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // the STEPS sub-steps of the chunk in (xa, xb); the last one decodes
+  // sub-step 0 of the chunk in (ya, yb)
+  auto chunk_next = [&](const OpA (&xa)[WM], const OpB (&xb)[WN], const OpA (&ya)[WM],
+                        const OpB (&yb)[WN]) {
+#pragma unroll
+    for (int s = 0; s < STEPS; s += 2) {
+      substep_next(xa, xb, s + 1, bv0, bv1);
+      if (s + 2 < STEPS) substep_next(xa, xb, s + 2, bv1, bv0);
+      else substep_next(ya, yb, 0, bv1, bv0);
+    }
+  };
+  auto chunk_last = [&](const OpA (&xa)[WM], const OpB (&xb)[WN]) {
+#pragma unroll
+    for (int s = 0; s < STEPS; s += 2) {
+      substep_next(xa, xb, s + 1, bv0, bv1);
+      if (s + 2 < STEPS) substep_next(xa, xb, s + 2, bv1, bv0);
+      else substep_last(bv1);
+    }
+  };
+
+  // nchunks >= 1; the loop body always has a chunk after the one it works on
+  const int nchunks = (int)(g.K / KC);
+  load_chunk(0, ra0, rb0);
+#pragma unroll
+  for (int i = 0; i < WM; ++i) av[i] = ra0[i].decode(0, lb_a);
+#pragma unroll
+  for (int j = 0; j < WN; ++j) bv0[j] = rb0[j].decode(0, lb_b);
+  int c = 0;
+  for (; c + 2 < nchunks; c += 2) {
+    load_chunk(c + 1, ra1, rb1);
+    chunk_next(ra0, rb0, ra1, rb1);
+    load_chunk(c + 2, ra0, rb0);
+    chunk_next(ra1, rb1, ra0, rb0);
+  }
+  if (c + 1 < nchunks) {  // two chunks left
+    load_chunk(c + 1, ra1, rb1);
+    chunk_next(ra0, rb0, ra1, rb1);
+    chunk_last(ra1, rb1);
+  } else {                // one chunk left
+    chunk_last(ra0, rb0);
+  }
+
+  // epilogue: block (j, i) of lane l holds weight rows
+  // n_base + 32 j + 8 qq + 4 half + 0..3 (qq < 4) of token m_base + 32 i + r32.
+  // Per run of four weight rows the factors r_n and the bias are read once
+  // and applied to all WM token blocks.  A wave whose outputs lie inside the
+  // matrix, with row length and pointers aligned for 8/16-byte accesses,
+  // takes the vector path with no per-element checks.
+  float sm[WM];
+#pragma unroll
+  for (int i = 0; i < WM; ++i) {
+    const long long m = m_base + 32 * i + r32;
+    sm[i] = (KIND == 0) ? g.s[m < g.M ? m : g.M - 1] * g.inv_k : 1.0f;
+  }
+  const bool f32_out = g.out_dtype != ORBIT_BF16;
+  const uintptr_t align_bits = (uintptr_t)g.out | (uintptr_t)g.r_bf16 | (uintptr_t)g.bias;
+  const bool fast = (g.N & 3) == 0 && (align_bits & 15) == 0 && m_base + TM / 2 <= g.M &&
+                    n_base + TN / 2 <= g.N;
+  // straight-line epilogue for one output type and bias kind (0 none,
+  // 1 bf16, 2 f32): every column factor is loaded first, then the outputs
+  // are scaled, rounded and stored four at a time
+  auto epi = [&](auto f32c, auto biasc) {
+    constexpr bool F32 = decltype(f32c)::value;
+    constexpr int BK = decltype(biasc)::value;
+    u32x2 rb[WN][4];
+    float4 cb[WN][4];
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const long long n0 = n_base + 32 * j + 8 * qq + 4 * half;
+        if constexpr (KIND == 0) rb[j][qq] = *(const u32x2*)(g.r_bf16 + n0);
+        if constexpr (BK == 1) {
+          const u32x2 bb = *(const u32x2*)((const uint16_t*)g.bias + n0);
+          cb[j][qq] = make_float4(__uint_as_float(bb.x << 16), __uint_as_float(bb.x & 0xffff0000u),
+                                  __uint_as_float(bb.y << 16), __uint_as_float(bb.y & 0xffff0000u));
+        } else if constexpr (BK == 2) {
+          cb[j][qq] = *(const float4*)((const float*)g.bias + n0);
+        } else {
+          cb[j][qq] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const long long n0 = n_base + 32 * j + 8 * qq + 4 * half;
+        float cf[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+        if constexpr (KIND == 0) {
+          cf[0] = __uint_as_float(rb[j][qq].x << 16);
+          cf[1] = __uint_as_float(rb[j][qq].x & 0xffff0000u);
+          cf[2] = __uint_as_float(rb[j][qq].y << 16);
+          cf[3] = __uint_as_float(rb[j][qq].y & 0xffff0000u);
+        }
+        const float cbv[4] = {cb[j][qq].x, cb[j][qq].y, cb[j][qq].z, cb[j][qq].w};
+#pragma unroll
+        for (int i = 0; i < WM; ++i) {
+          const long long m = m_base + 32 * i + r32;
+          float y[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) y[q] = __builtin_fmaf(acc[j][i][4 * qq + q], sm[i] * cf[q], cbv[q]);
+          if constexpr (F32) {
+            *(float4*)((float*)g.out + m * g.N + n0) = make_float4(y[0], y[1], y[2], y[3]);
+          } else {
+            u32x2 w;
+            w.x = pack_bf16x2(y[0], y[1]);
+            w.y = pack_bf16x2(y[2], y[3]);
+            *(u32x2*)((uint16_t*)g.out + m * g.N + n0) = w;
+          }
+        }
+      }
+    }
+  };
+  if (fast) {
+    using T = std::true_type;
+    using F = std::false_type;
+    const int bk = !g.bias ? 0 : (g.bias_dtype == ORBIT_BF16 ? 1 : 2);
+    if (f32_out) {
+      if (bk == 0) epi(T{}, std::integral_constant<int, 0>{});
+      else if (bk == 1) epi(T{}, std::integral_constant<int, 1>{});
+      else epi(T{}, std::integral_constant<int, 2>{});
+    } else {
+      if (bk == 0) epi(F{}, std::integral_constant<int, 0>{});
+      else if (bk == 1) epi(F{}, std::integral_constant<int, 1>{});
+      else epi(F{}, std::integral_constant<int, 2>{});
+    }
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < WN; ++j) {
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const long long n = n_base + 32 * j + 8 * qq + 4 * half + q;
+        if (n >= g.N) continue;
+        const float cf = (KIND == 0) ? __uint_as_float((uint32_t)g.r_bf16[n] << 16) : 1.0f;
+        const float cb = load_bias(g, n);
+#pragma unroll
+        for (int i = 0; i < WM; ++i) {
+          const long long m = m_base + 32 * i + r32;
+          if (m >= g.M) continue;
+          const float y = __builtin_fmaf(acc[j][i][4 * qq + q], sm[i] * cf, cb);
+          if (f32_out) ((float*)g.out)[m * g.N + n] = y;
+          else ((uint16_t*)g.out)[m * g.N + n] = f32_to_bf16_rne(y);
+        }
+      }
+    }
+  }
+}
+
+template <int KIND, class OpA, class OpB, int WM, int WN>
+hipError_t launch_tile(GemmArgs& g, int lds, hipStream_t stream) {
+  constexpr int TM = 64 * WM, TN = 64 * WN;
+  g.tiles_m = (int)((g.M + TM - 1) / TM);
+  g.tiles_n = (int)((g.N + TN - 1) / TN);
+  const long long tiles = (long long)g.tiles_m * g.tiles_n;
+  if (tiles == 0) return hipSuccess;
+  if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
+  auto kern = gemm_kernel<KIND, OpA, OpB, WM, WN>;
+  static LaunchCache cache;
+  hipError_t e = prepare_launch(cache, (const void*)kern, 256, lds, nullptr);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(256), lds, stream, g);
+  return hipGetLastError();
+}
+
+// Picks the tile: large tiles when there are enough of them to fill the
+// 256 compute units, smaller ones otherwise.
+template <int KIND, class OpA, class OpB>
+hipError_t launch_shape(GemmArgs& g, int lds, hipStream_t stream) {
+  auto tiles = [&](int tm, int tn) { return ((g.M + tm - 1) / tm) * ((g.N + tn - 1) / tn); };
+  if (tiles(256, 192) >= 192) return launch_tile<KIND, OpA, OpB, 4, 3>(g, lds, stream);
+  if (tiles(128, 128) >= 128) return launch_tile<KIND, OpA, OpB, 2, 2>(g, lds, stream);
+  return launch_tile<KIND, OpA, OpB, 1, 1>(g, lds, stream);
+}
+
+// LDS layout of the two decode tables.  Tables addressed through v_perm
+// (2-, 4- and 8-bit codes, 64 KB each) must start at a multiple of 64 KB,
+// so a 64 KB table goes first; 3- and 6-bit tables (16 KB) only need 16 KB
+// alignment.  A shared codebook uses one table.
+template <int BA, int BB>
+hipError_t launch_codes(GemmArgs& g, hipStream_t stream, bool same_table) {
+  const int tab_a = CodeOp<BA>::kTableBytes, tab_b = CodeOp<BB>::kTableBytes;
+  int lds;
+  if (same_table) {
+    g.table_a_offset = 0;
+    g.table_b_offset = 0;
+    lds = tab_a;
+  } else if (tab_a >= tab_b) {
+    g.table_a_offset = 0;
+    g.table_b_offset = tab_a;
+    lds = tab_a + tab_b;
+  } else {
+    g.table_b_offset = 0;
+    g.table_a_offset = tab_b;
+    lds = tab_a + tab_b;
+  }
+  return launch_shape<0, CodeOp<BA>, CodeOp<BB>>(g, lds, stream);
+}
+
+// Defined (and instantiated) in qgemm_a<BA>.hip, one translation unit per
+// activation width so the kernels compile in parallel.
+template <int BA>
+hipError_t launch_codes_b(GemmArgs& g, int bb, hipStream_t stream, bool same);
+
+#define ORBIT_DEFINE_LAUNCH_CODES_B(BA)                                          \
+  template <>                                                                   \
+  hipError_t launch_codes_b<BA>(GemmArgs & g, int bb, hipStream_t stream, bool same) { \
+    switch (bb) {                                                               \
+      case 2: return launch_codes<BA, 2>(g, stream, false);                     \
+      case 3: return launch_codes<BA, 3>(g, stream, false);                     \
+      case 4: return launch_codes<BA, 4>(g, stream, same && BA == 4);           \
+      case 6: return launch_codes<BA, 6>(g, stream, false);                     \
+      case 8: return launch_codes<BA, 8>(g, stream, same && BA == 8);           \
+    }                                                                           \
+    return hipErrorInvalidValue;                                                \
+  }
+
+hipError_t launch_int8(GemmArgs& g, hipStream_t stream);
+
+}  // namespace qgemm
+}  // namespace orbit

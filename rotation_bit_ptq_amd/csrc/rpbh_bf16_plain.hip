@@ -1,0 +1,10 @@
+// Rotation-only and int8-pack kernels for bf16 rows (see rpbh_impl.h).
+#include "rpbh_impl.h"
+
+namespace orbit {
+namespace rows {
+ORBIT_ROWS_PLAIN_MODE(uint16_t, kRotF32)
+ORBIT_ROWS_PLAIN_MODE(uint16_t, kRotF16)
+ORBIT_ROWS_PLAIN_MODE(uint16_t, kInt8)
+}  // namespace rows
+}  // namespace orbit

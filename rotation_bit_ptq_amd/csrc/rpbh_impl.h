@@ -1,0 +1,680 @@
+// Fused RPBH rotate (+ norm split, codebook quantize, pack) over rows.
+//
+// OrbitQuant page, Method: x' = Pi_d x with Pi_d = blkdiag(H_h D_i) P_pi;
+// s = ||x'||; the direction x'/(s + eps) is quantized by the Lloyd-Max
+// codebook; weights go through the same rotation offline (W' = W Pi^T, one
+// row at a time) with their norm kept in BF16.  The int8 article's packer
+// (section 4: rotate, per-group scale, round) and the plain rotation reuse
+// the same front end.
+//
+// Layout of the work (gfx950, wave64):
+//   * one wave owns one row (token or weight row) at a time and loops over
+//     rows with a grid stride, with the next row's HBM loads in flight while
+//     the current row is transformed; no workgroup barriers on the row path;
+//   * the row lands in the wave's LDS buffer twice, as x and as -x, so the
+//     Rademacher sign of permuted coordinate k is part of its gather address:
+//       y_k = D_k x[pi(k)] = buf[pi(k) + (D_k < 0 ? d : 0)];
+//     the addresses are computed once per wave and stay in registers;
+//   * lane-slot j holds rotated coordinates 16 j .. 16 j + 15: for bf16 rows
+//     two gathered neighbours share a register and one v_dot2_f32_bf16 with
+//     (1, 1) or (1, -1) gives the first butterfly stage already in fp32; the
+//     next three stages run in registers and the remaining log2(h) - 4
+//     stages pair lanes j and j ^ 2^s through DPP moves (xor 1, 2, 8) or
+//     ds_swizzle (xor 4, 16);
+//   * the squared norm is reduced across the wave; the quantizer counts the
+//     thresholds below u with one lookup in a uniform grid over u: each cell
+//     holds at most one threshold, so idx = base[cell] + (t[cell] < u), the
+//     same float32 decision as a full count.  The cell index is read off the
+//     bits of fma(u, a, b + 2^23) (a monotone rounding), clamped by v_med3;
+//   * each lane writes its 16 codes as one 2*bits-byte word.
+// Rows with d <= 4096 keep their rotated values and gather addresses in
+// registers (one pass over LDS); longer rows make two passes (norm, then
+// quantize) over the LDS copy, so HBM is still read once.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+
+#include "orbit_internal.h"
+
+namespace orbit {
+namespace rows {
+
+constexpr int kWave = 64;
+constexpr int kSlot = 16;  // rotated coordinates per lane-slot
+constexpr int kMaxCachedRounds = 4;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+struct RowArgs {
+  int d, h, log2h, nslots, nrounds;
+  long long rows;
+  const int32_t* perm;
+  const uint32_t* sign_bits;
+  const void* in;
+  float sqrt_d_over_h;  // sqrt(d / h): u = z * sqrt(d/h) / (s + eps), z = H y unnormalised
+  float inv_sqrt_h;
+  float inv_h;
+  float eps;
+  float ga, gb;  // gb already includes 2^23
+  int cells, nthr;
+  uint32_t grid_bias;  // 0xA8000000: turns the cell's float bits into its byte offset
+  float thr[ORBIT_MAX_LEVELS - 1];
+  uint8_t* idx_out;
+  float* s_out;
+  uint16_t* r_out;
+  float* xrot_f32;
+  uint16_t* xrot_f16;
+  int group;
+  int8_t* q_out;
+  uint16_t* scale_out;
+  int grid_bytes;   // LDS bytes of the grid table
+  int row_bytes;    // LDS bytes of one wave's row buffer (x and -x)
+  int wave_bytes;   // row buffer + transpose scratch of one wave
+};
+
+enum Mode { kAct = 0, kWeight = 1, kRotF32 = 2, kRotF16 = 3, kInt8 = 4 };
+
+struct GridCell {
+  float t;   // the threshold inside the cell, +inf if none
+  int base;  // thresholds in lower cells
+};
+
+constexpr float kMagic = 8388608.0f;  // 2^23: floats in [2^23, 2^24) are integers
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_rne(float f) {
+  _Float16 h = (_Float16)f;  // v_cvt_f16_f32: round to nearest even
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+// The grid cell of u: the float fma(u, a, b + 2^23) rounded to an integer,
+// clamped to [2^23, 2^23 + cells - 1]; returns the cell's LDS byte address
+// (the grid table starts at LDS byte 0, 8 bytes per cell):
+// (bits - 0x4B000000) * 8 = bits * 8 + bias, bias = 0xA8000000 (mod 2^32),
+// passed in as a kernel argument so it sits in a scalar register.
+__device__ __forceinline__ uint32_t grid_addr(float u, float a, float b, float top, uint32_t bias) {
+  float f = __builtin_fmaf(u, a, b);
+  f = __builtin_amdgcn_fmed3f(f, kMagic, top);
+  return (__float_as_uint(f) << 3) + bias;
+}
+
+__device__ __forceinline__ int grid_index(float u, float a, float b, float top) {
+  float f = __builtin_amdgcn_fmed3f(__builtin_fmaf(u, a, b), kMagic, top);
+  return (int)(__float_as_uint(f) - 0x4B000000u);
+}
+
+// Sum over the wave, identical in every lane and independent of timing:
+// DPP butterflies inside each row of 16 lanes, then the four row sums are
+// read as scalars and added in a fixed order.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));   // xor 1
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));   // xor 2
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));  // half-row mirror
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true));  // row mirror
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+__device__ __forceinline__ float group_max(float v, int lanes) {
+  for (int m = 1; m < lanes; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+
+// Orders a wave's LDS writes before its later reads (a wave's LDS
+// operations complete in order; this keeps the compiler from moving them).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Value of lane ^ M.
+template <int M>
+__device__ __forceinline__ float xor_partner(float v) {
+  const int x = __float_as_int(v);
+  if constexpr (M == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true));
+  if constexpr (M == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true));
+  if constexpr (M == 4) return __int_as_float(__builtin_amdgcn_ds_swizzle(x, 0x101F));
+  if constexpr (M == 8) return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, true));
+  if constexpr (M == 16) return __int_as_float(__builtin_amdgcn_ds_swizzle(x, 0x401F));
+  if constexpr (M == 32) return __shfl_xor(v, 32, kWave);
+  return v;
+}
+
+// Butterfly between lanes j and j ^ M: the lower lane keeps a + b, the
+// upper one a - b (its partner holds a).  Written as partner + v * sign with
+// contraction off, so the DPP move folds into the add's source operand and
+// the add's result may land in any register.
+template <int M>
+__device__ __forceinline__ void lane_stage(float (&v)[kSlot], int lane) {
+#pragma clang fp contract(off)
+  const float sg = (lane & M) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int i = 0; i < kSlot; ++i) {
+    const float t = v[i] * sg;
+    v[i] = xor_partner<M>(v[i]) + t;
+  }
+}
+
+__device__ __forceinline__ void lane_stages(float (&v)[kSlot], int lane, int nstages) {
+  if (nstages > 0) lane_stage<1>(v, lane);
+  if (nstages > 1) lane_stage<2>(v, lane);
+  if (nstages > 2) lane_stage<4>(v, lane);
+  if (nstages > 3) lane_stage<8>(v, lane);
+  if (nstages > 4) lane_stage<16>(v, lane);
+  if (nstages > 5) lane_stage<32>(v, lane);
+}
+
+// Butterfly stages of span `from` .. 8 inside the lane's 16 values.
+__device__ __forceinline__ void slot_stages(float (&v)[kSlot], int from) {
+#pragma unroll
+  for (int span = 1; span < kSlot; span <<= 1) {
+    if (span < from) continue;
+#pragma unroll
+    for (int i = 0; i < kSlot; ++i) {
+      if ((i & span) == 0) {
+        float x = v[i], y = v[i + span];
+        v[i] = x + y;
+        v[i + span] = x - y;
+      }
+    }
+  }
+}
+
+template <typename InT>
+__device__ __forceinline__ float lds_value(const char* smem, uint32_t addr) {
+  if constexpr (sizeof(InT) == 2) return __uint_as_float((uint32_t)(*(const uint16_t*)(smem + addr)) << 16);
+  else return *(const float*)(smem + addr);
+}
+
+// Gathers the lane's 16 permuted, signed coordinates and applies H_16.
+template <typename InT>
+__device__ __forceinline__ void gather_h16(const char* smem, const uint32_t (&addr)[kSlot],
+                                           float (&v)[kSlot]) {
+#pragma unroll
+  for (int i = 0; i < kSlot; ++i) v[i] = lds_value<InT>(smem, addr[i]);
+  slot_stages(v, 1);
+}
+
+// LDS byte addresses of y_k = D_k x[pi(k)] for k = 16 slot .. 16 slot + 15.
+template <typename InT>
+__device__ __forceinline__ void slot_addresses(const RowArgs& a, int slot, uint32_t wbuf,
+                                               uint32_t (&addr)[kSlot]) {
+  const int k0 = (slot < a.nslots ? slot : 0) * kSlot;
+  const i32x4* pp = (const i32x4*)(a.perm + k0);
+  const i32x4 p0 = pp[0], p1 = pp[1], p2 = pp[2], p3 = pp[3];
+  const uint32_t sw = a.sign_bits[k0 >> 5] >> (k0 & 31);  // 16 signs (k0 % 16 == 0)
+  const int p[kSlot] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w,
+                        p2.x, p2.y, p2.z, p2.w, p3.x, p3.y, p3.z, p3.w};
+#pragma unroll
+  for (int i = 0; i < kSlot; ++i)
+    addr[i] = wbuf + ((uint32_t)p[i] + ((sw >> i) & 1u) * (uint32_t)a.d) * (uint32_t)sizeof(InT);
+}
+
+// ---- transposed gather (h = 16 T, T = 2^LT lanes per Hadamard block) ----
+// Position p of a block is split as p = 16 t + i (t < T, i < 16); since
+// H_h = H_T (x) H_16 in Sylvester order, the transform is H_T over t for
+// every i, then H_16 over i for every t.  Lane t' of the block's T lanes
+// first gathers p = 16 t + G t' + i' (all t, i' < G = 16 / T) and runs H_T
+// in registers; one pass through a per-wave LDS scratch then hands every
+// lane its 16 consecutive positions 16 t' .. 16 t' + 15 for H_16, again in
+// registers.  Every butterfly stage is a register add/sub.
+template <int LT>
+struct TrShape {
+  static constexpr int T = 1 << LT;       // lanes per block
+  static constexpr int G = 16 >> LT;      // i values per lane before the transpose
+  static constexpr int LG = 4 - LT;       // element bits that index i'
+  static constexpr int P = 20;            // scratch words per lane (16 + 4 padding)
+  static constexpr int S = P * T + 4;     // scratch words per block
+  static constexpr int kScratchBytes = (kWave / T) * S * 4;
+};
+
+// Permuted index k of element e = t G + i' of the lane's gather.
+template <int LT>
+__device__ __forceinline__ int tr_k(int slot, int e) {
+  using Sh = TrShape<LT>;
+  const int tp = slot & (Sh::T - 1);
+  return (slot - tp) * kSlot + kSlot * (e >> Sh::LG) + Sh::G * tp + (e & (Sh::G - 1));
+}
+
+template <typename InT, int LT>
+__device__ __forceinline__ void tr_addresses(const RowArgs& a, int slot, uint32_t wbuf,
+                                             uint32_t (&addr)[kSlot]) {
+  const int s = slot < a.nslots ? slot : 0;
+#pragma unroll
+  for (int e = 0; e < kSlot; ++e) {
+    const int k = tr_k<LT>(s, e);
+    const uint32_t p = (uint32_t)a.perm[k];
+    const uint32_t neg = (a.sign_bits[k >> 5] >> (k & 31)) & 1u;
+    addr[e] = wbuf + (p + neg * (uint32_t)a.d) * (uint32_t)sizeof(InT);
+  }
+}
+
+// Butterflies over element-index bits [lo, 4) (bit b pairs e and e ^ 2^b).
+template <int LO>
+__device__ __forceinline__ void elem_stages(float (&v)[kSlot]) {
+#pragma unroll
+  for (int span = 1 << LO; span < kSlot; span <<= 1) {
+#pragma unroll
+    for (int e = 0; e < kSlot; ++e) {
+      if ((e & span) == 0) {
+        float x = v[e], y = v[e + span];
+        v[e] = x + y;
+        v[e + span] = x - y;
+      }
+    }
+  }
+}
+
+// Gather, H_T, transpose, H_16: v ends as the lane's 16 consecutive
+// positions of x' (unnormalised).  `scr` is the wave scratch's byte offset.
+template <typename InT, int LT>
+__device__ __forceinline__ void tr_rotate(char* smem, uint32_t scr, const uint32_t (&addr)[kSlot],
+                                          float (&v)[kSlot], int lane) {
+  using Sh = TrShape<LT>;
+#pragma unroll
+  for (int e = 0; e < kSlot; ++e) v[e] = lds_value<InT>(smem, addr[e]);
+  elem_stages<Sh::LG>(v);  // H_T over t = e >> LG
+  const int tp = lane & (Sh::T - 1);
+  const uint32_t grp = scr + (uint32_t)((lane >> LT) * Sh::S) * 4u;
+  // writer layout: word P tp + e of the block's scratch.  A padded lane
+  // stride of 20 words puts the lanes of a block on distinct bank quads and
+  // the block stride S shifts blocks against each other.  The reads below
+  // follow the writes in program order; a wave's LDS operations complete in
+  // order and the two address sets may alias, so they are not reordered.
+  float4* w = (float4*)(smem + grp + 4u * Sh::P * (uint32_t)tp);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) w[j] = make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
+  // position 16 tp + G tq + i' sits in writer tq's element tp G + i'
+  const char* rd = smem + grp + 4u * (uint32_t)(Sh::G * tp);
+#pragma unroll
+  for (int tq = 0; tq < Sh::T; ++tq) {
+    const float* src = (const float*)(rd + 4 * Sh::P * tq);
+    if constexpr (Sh::G == 4) {
+      float4 q = *(const float4*)src;
+      v[4 * tq] = q.x; v[4 * tq + 1] = q.y; v[4 * tq + 2] = q.z; v[4 * tq + 3] = q.w;
+    } else if constexpr (Sh::G == 2) {
+      float2 q = *(const float2*)src;
+      v[2 * tq] = q.x; v[2 * tq + 1] = q.y;
+    } else {
+      v[tq] = src[0];
+    }
+  }
+  elem_stages<0>(v);       // H_16 over i
+}
+
+template <int BITS>
+__device__ __forceinline__ void store_indices(uint8_t* row_out, int slot, const int (&idx)[kSlot]) {
+  constexpr int kWords = (kSlot * BITS + 31) / 32;
+  uint32_t w[kWords];
+#pragma unroll
+  for (int i = 0; i < kWords; ++i) w[i] = 0;
+#pragma unroll
+  for (int i = 0; i < kSlot; ++i) {
+    const int bit = i * BITS;
+    w[bit / 32] |= (uint32_t)idx[i] << (bit % 32);
+    if ((bit % 32) + BITS > 32) w[bit / 32 + 1] |= (uint32_t)idx[i] >> (32 - bit % 32);
+  }
+  uint8_t* p = row_out + (size_t)slot * (2 * BITS);
+  if constexpr (BITS == 8) {
+    *(uint4*)p = make_uint4(w[0], w[1], w[2], w[3]);
+  } else if constexpr (BITS == 4) {
+    *(uint2*)p = make_uint2(w[0], w[1]);
+  } else if constexpr (BITS == 2) {
+    *(uint32_t*)p = w[0];
+  } else if constexpr (BITS == 6) {
+    uint32_t* q = (uint32_t*)p;  // 12-byte words, 4-byte aligned
+    q[0] = w[0];
+    q[1] = w[1];
+    q[2] = w[2];
+  } else if constexpr (BITS == 3) {
+    uint16_t* q = (uint16_t*)p;  // 6-byte words, 2-byte aligned
+    q[0] = (uint16_t)w[0];
+    q[1] = (uint16_t)(w[0] >> 16);
+    q[2] = (uint16_t)w[1];
+  } else {
+    static_assert(BITS == 1, "unsupported width");
+    *(uint16_t*)p = (uint16_t)w[0];
+  }
+}
+
+// A row in flight: the lane's 16-byte chunks c = lane + 64 j.
+template <typename InT, int NCH>
+struct RowRegs {
+  u32x4 c[NCH];
+
+  __device__ __forceinline__ void load(const RowArgs& a, long long row, int lane) {
+    const int nchunk = a.d * (int)sizeof(InT) / 16;
+    const u32x4* src = (const u32x4*)((const char*)a.in + (size_t)row * a.d * sizeof(InT));
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int ch = lane + kWave * j;
+      c[j] = __builtin_nontemporal_load(src + (ch < nchunk ? ch : 0));
+    }
+  }
+
+  // writes x and -x into the wave's buffer
+  __device__ __forceinline__ void store(const RowArgs& a, char* smem, uint32_t wbuf, int lane) const {
+    const int nchunk = a.d * (int)sizeof(InT) / 16;
+    const uint32_t negoff = (uint32_t)a.d * (uint32_t)sizeof(InT);
+    const uint32_t flip = sizeof(InT) == 2 ? 0x80008000u : 0x80000000u;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int ch = lane + kWave * j;
+      if (ch < nchunk) {
+        *(u32x4*)(smem + wbuf + ch * 16) = c[j];
+        *(u32x4*)(smem + wbuf + negoff + ch * 16) = c[j] ^ flip;
+      }
+    }
+  }
+};
+
+template <int MODE, int BITS>
+__device__ __forceinline__ void emit_slot(const RowArgs& a, long long row, int slot, int lane,
+                                          float (&v)[kSlot], float alpha, const char* smem) {
+  const int d = a.d;
+  if constexpr (MODE == kAct || MODE == kWeight) {
+    const float top = kMagic + (float)(a.cells - 1);
+    int idx[kSlot];
+#pragma unroll
+    for (int i = 0; i < kSlot; ++i) {
+      const float u = v[i] * alpha;
+      const GridCell g = *(const GridCell*)(smem + grid_addr(u, a.ga, a.gb, top, a.grid_bias));
+      idx[i] = g.base + (g.t < u ? 1 : 0);
+    }
+    store_indices<BITS>(a.idx_out + (size_t)row * ((size_t)d * BITS / 8), slot, idx);
+    if (MODE == kAct && a.xrot_f32) {
+      float4* o = (float4*)(a.xrot_f32 + (size_t)row * d + slot * kSlot);
+#pragma unroll
+      for (int i = 0; i < kSlot; i += 4)
+        o[i / 4] = make_float4(v[i] * a.inv_sqrt_h, v[i + 1] * a.inv_sqrt_h,
+                               v[i + 2] * a.inv_sqrt_h, v[i + 3] * a.inv_sqrt_h);
+    }
+  } else if constexpr (MODE == kRotF32) {
+    float4* o = (float4*)(a.xrot_f32 + (size_t)row * d + slot * kSlot);
+#pragma unroll
+    for (int i = 0; i < kSlot; i += 4)
+      o[i / 4] = make_float4(v[i] * a.inv_sqrt_h, v[i + 1] * a.inv_sqrt_h,
+                             v[i + 2] * a.inv_sqrt_h, v[i + 3] * a.inv_sqrt_h);
+  } else if constexpr (MODE == kRotF16) {
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      w[i] = (uint32_t)f32_to_f16_rne(v[2 * i] * a.inv_sqrt_h) |
+             ((uint32_t)f32_to_f16_rne(v[2 * i + 1] * a.inv_sqrt_h) << 16);
+    uint4* o = (uint4*)(a.xrot_f16 + (size_t)row * d + slot * kSlot);
+    o[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    o[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  } else {  // kInt8: per-group symmetric scale, round half to even
+    float w[kSlot];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kSlot; ++i) {
+      w[i] = v[i] * a.inv_sqrt_h;
+      amax = fmaxf(amax, fabsf(w[i]));
+    }
+    const int lanes = a.group / kSlot;  // lanes per group, a power of two <= 64
+    amax = group_max(amax, lanes);
+    const uint16_t sbits = f32_to_f16_rne(amax / 127.0f);
+    const float sc = (float)__builtin_bit_cast(_Float16, sbits);
+    uint32_t q4[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < kSlot; ++i) {
+      float qf = 0.0f;
+      if (sc > 0.0f) qf = fminf(fmaxf(__builtin_rintf(w[i] / sc), -127.0f), 127.0f);
+      q4[i / 4] |= ((uint32_t)(int)qf & 0xffu) << (8 * (i % 4));
+    }
+    *(uint4*)(a.q_out + (size_t)row * d + slot * kSlot) = make_uint4(q4[0], q4[1], q4[2], q4[3]);
+    if ((lane & (lanes - 1)) == 0)
+      a.scale_out[(size_t)row * (d / a.group) + slot * kSlot / a.group] = sbits;
+  }
+}
+
+template <int MODE>
+__device__ __forceinline__ float row_alpha(const RowArgs& a, float ss, long long row, int lane) {
+  if constexpr (MODE == kAct) {
+    float s = sqrtf(ss * a.inv_h);
+    if (lane == 0) a.s_out[row] = s;
+    return a.sqrt_d_over_h / (s + a.eps);
+  } else if constexpr (MODE == kWeight) {
+    float r = sqrtf(ss * a.inv_h);
+    if (lane == 0) a.r_out[row] = f32_to_bf16_rne(r);
+    return r > 0.0f ? a.sqrt_d_over_h / r : 0.0f;
+  } else {
+    return 0.0f;
+  }
+}
+
+// Grid table: cell c holds the unique threshold the float32 classification
+// puts in it (if any) and the number of thresholds in lower cells.  The
+// thresholds are read in a uniform loop (scalar loads from the kernel
+// arguments), never with per-lane indices.
+__device__ __forceinline__ void build_grid(const RowArgs& a, char* smem) {
+  const float top = kMagic + (float)(a.cells - 1);
+  for (int c = threadIdx.x; c < a.cells; c += blockDim.x) {
+    GridCell g;
+    g.base = 0;
+    g.t = INFINITY;
+    for (int j = 0; j < a.nthr; ++j) {
+      const float t = a.thr[j];
+      const int cj = grid_index(t, a.ga, a.gb, top);
+      g.base += (cj < c) ? 1 : 0;
+      if (cj == c) g.t = t;
+    }
+    ((GridCell*)smem)[c] = g;
+  }
+}
+
+// R > 0: rows of at most 1024 R coordinates, values and addresses in
+// registers.  R == 0: longer rows, two passes over the LDS copy.
+// LT >= 0: transposed gather with T = 2^LT lanes per Hadamard block (h =
+// 16 T); LT < 0: consecutive gather with cross-lane butterfly stages.
+template <typename InT, int MODE, int BITS, int R, int LT>
+__global__ __launch_bounds__(256) void rows_kernel(RowArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int waves = blockDim.x / kWave;
+  const uint32_t wbuf = (uint32_t)(a.grid_bytes + wave * a.wave_bytes);
+  const uint32_t scr = wbuf + (uint32_t)a.row_bytes;  // transpose scratch (LT >= 0)
+  const long long stride = (long long)gridDim.x * waves;
+  long long row = (long long)blockIdx.x * waves + wave;
+  const int nstages = a.log2h - 4;
+  constexpr bool kQuant = (MODE == kAct || MODE == kWeight);
+
+  if constexpr (R > 0) {
+    constexpr int NCH = R * (int)sizeof(InT);  // 16-byte chunks per lane
+    RowRegs<InT, NCH> pre;
+    if (row < a.rows) pre.load(a, row, lane);
+    uint32_t addr[R][kSlot];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if constexpr (LT >= 0) tr_addresses<InT, LT>(a, r * kWave + lane, wbuf, addr[r]);
+      else slot_addresses<InT>(a, r * kWave + lane, wbuf, addr[r]);
+    }
+    if constexpr (kQuant) {
+      build_grid(a, smem);
+      __syncthreads();
+    }
+    for (; row < a.rows; row += stride) {
+      pre.store(a, smem, wbuf, lane);
+      if (row + stride < a.rows) pre.load(a, row + stride, lane);
+      wave_lds_sync();
+      float v[R][kSlot];
+      float ss = 0.0f;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if constexpr (LT >= 0) {
+          tr_rotate<InT, LT>(smem, scr, addr[r], v[r], lane);
+        } else {
+          gather_h16<InT>(smem, addr[r], v[r]);
+          lane_stages(v[r], lane, nstages);
+        }
+        if (r * kWave + lane < a.nslots) {
+#pragma unroll
+          for (int i = 0; i < kSlot; ++i) ss = __builtin_fmaf(v[r][i], v[r][i], ss);
+        }
+      }
+      wave_lds_sync();  // every lane has gathered before the next row lands
+      if constexpr (kQuant) ss = wave_sum(ss);
+      const float alpha = row_alpha<MODE>(a, ss, row, lane);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int slot = r * kWave + lane;
+        if (slot < a.nslots) emit_slot<MODE, BITS>(a, row, slot, lane, v[r], alpha, smem);
+      }
+    }
+  } else {
+    if constexpr (kQuant) {
+      build_grid(a, smem);
+      __syncthreads();
+    }
+    const int nchunk = a.d * (int)sizeof(InT) / 16;
+    const uint32_t negoff = (uint32_t)a.d * (uint32_t)sizeof(InT);
+    const uint32_t flip = sizeof(InT) == 2 ? 0x80008000u : 0x80000000u;
+    for (; row < a.rows; row += stride) {
+      const u32x4* src = (const u32x4*)((const char*)a.in + (size_t)row * a.d * sizeof(InT));
+      for (int ch = lane; ch < nchunk; ch += kWave) {
+        u32x4 x = __builtin_nontemporal_load(src + ch);
+        *(u32x4*)(smem + wbuf + ch * 16) = x;
+        *(u32x4*)(smem + wbuf + negoff + ch * 16) = x ^ flip;
+      }
+      wave_lds_sync();
+      float ss = 0.0f, alpha = 0.0f;
+      for (int pass = kQuant ? 0 : 1; pass < 2; ++pass) {
+        for (int r = 0; r < a.nrounds; ++r) {
+          const int slot = r * kWave + lane;
+          uint32_t addr[kSlot];
+          float v[kSlot];
+          if constexpr (LT >= 0) {
+            tr_addresses<InT, LT>(a, slot, wbuf, addr);
+            tr_rotate<InT, LT>(smem, scr, addr, v, lane);
+          } else {
+            slot_addresses<InT>(a, slot, wbuf, addr);
+            gather_h16<InT>(smem, addr, v);
+            lane_stages(v, lane, nstages);
+          }
+          if (slot < a.nslots) {
+            if (pass == 0) {
+#pragma unroll
+              for (int i = 0; i < kSlot; ++i) ss = __builtin_fmaf(v[i], v[i], ss);
+            } else {
+              emit_slot<MODE, BITS>(a, row, slot, lane, v, alpha, smem);
+            }
+          }
+        }
+        if (pass == 0) {
+          ss = wave_sum(ss);
+          alpha = row_alpha<MODE>(a, ss, row, lane);
+        }
+      }
+      wave_lds_sync();
+    }
+  }
+}
+
+template <typename InT, int MODE, int BITS, int R, int LT>
+hipError_t launch_typed(RowArgs a, hipStream_t stream) {
+  DeviceInfo di;
+  hipError_t e = device_info(&di);
+  if (e != hipSuccess) return e;
+  if constexpr (LT >= 0) a.wave_bytes = a.row_bytes + TrShape<LT>::kScratchBytes;
+  else a.wave_bytes = a.row_bytes;
+  int waves = 4;
+  while (waves > 1 && a.grid_bytes + waves * a.wave_bytes > di.max_lds) waves >>= 1;
+  const int lds = a.grid_bytes + waves * a.wave_bytes;
+  if (lds > di.max_lds) return hipErrorInvalidValue;
+  auto kern = rows_kernel<InT, MODE, BITS, R, LT>;
+  static LaunchCache cache;
+  int per_cu = 1;
+  e = prepare_launch(cache, (const void*)kern, waves * kWave, lds, &per_cu);
+  if (e != hipSuccess) return e;
+  const long long need = (a.rows + waves - 1) / waves;
+  const long long cap = (long long)di.n_cu * per_cu;
+  const int blocks = (int)(need < cap ? need : cap);
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(waves * kWave), lds, stream, a);
+  return hipGetLastError();
+}
+
+// Register-resident rounds for a row of d coordinates (0 = two-pass path).
+inline int rounds_for(int d) {
+  const int r = (d / kSlot + kWave - 1) / kWave;
+  return r <= kMaxCachedRounds ? r : 0;
+}
+
+template <typename InT, int MODE, int BITS>
+hipError_t launch_rounds(const RowArgs& a, hipStream_t stream) {
+  switch (rounds_for(a.d)) {
+    case 1: return launch_typed<InT, MODE, BITS, 1, -1>(a, stream);
+    case 2: return launch_typed<InT, MODE, BITS, 2, -1>(a, stream);
+    case 3: return launch_typed<InT, MODE, BITS, 3, -1>(a, stream);
+    case 4: return launch_typed<InT, MODE, BITS, 4, -1>(a, stream);
+    default: return launch_typed<InT, MODE, BITS, 0, -1>(a, stream);
+  }
+}
+
+// Transposed-gather kernels for bf16 rows, h = 16 * 2^LT; rows of up to
+// 2048 coordinates share the two-round instantiation.
+template <int MODE, int BITS, int LT>
+hipError_t launch_fast_rounds(const RowArgs& a, hipStream_t stream) {
+  const int r = rounds_for(a.d);
+  if (r == 1 || r == 2) return launch_typed<uint16_t, MODE, BITS, 2, LT>(a, stream);
+  if (r == 3) return launch_typed<uint16_t, MODE, BITS, 3, LT>(a, stream);
+  if (r == 4) return launch_typed<uint16_t, MODE, BITS, 4, LT>(a, stream);
+  return launch_typed<uint16_t, MODE, BITS, 0, LT>(a, stream);
+}
+
+template <int MODE, int LT>
+hipError_t launch_fast(const RowArgs& a, int bits, hipStream_t stream);
+
+#define ORBIT_ROWS_FAST(MODE, LT)                                             \
+  template <>                                                               \
+  hipError_t launch_fast<MODE, LT>(const RowArgs& a, int bits, hipStream_t s) { \
+    switch (bits) {                                                         \
+      case 2: return launch_fast_rounds<MODE, 2, LT>(a, s);                 \
+      case 3: return launch_fast_rounds<MODE, 3, LT>(a, s);                 \
+      case 4: return launch_fast_rounds<MODE, 4, LT>(a, s);                 \
+      case 6: return launch_fast_rounds<MODE, 6, LT>(a, s);                 \
+      case 8: return launch_fast_rounds<MODE, 8, LT>(a, s);                 \
+    }                                                                       \
+    return hipErrorInvalidValue;                                            \
+  }
+
+// Instantiated per (input type, mode) in the rpbh_*.hip files.
+template <typename InT, int MODE>
+hipError_t launch_mode(const RowArgs& a, int bits, hipStream_t stream);
+
+#define ORBIT_ROWS_QUANT_MODE(InT, MODE)                                     \
+  template <>                                                               \
+  hipError_t launch_mode<InT, MODE>(const RowArgs& a, int bits, hipStream_t s) { \
+    switch (bits) {                                                         \
+      case 1: return launch_rounds<InT, MODE, 1>(a, s);                     \
+      case 2: return launch_rounds<InT, MODE, 2>(a, s);                     \
+      case 3: return launch_rounds<InT, MODE, 3>(a, s);                     \
+      case 4: return launch_rounds<InT, MODE, 4>(a, s);                     \
+      case 6: return launch_rounds<InT, MODE, 6>(a, s);                     \
+      case 8: return launch_rounds<InT, MODE, 8>(a, s);                     \
+    }                                                                       \
+    return hipErrorInvalidValue;                                            \
+  }
+
+#define ORBIT_ROWS_PLAIN_MODE(InT, MODE)                                     \
+  template <>                                                               \
+  hipError_t launch_mode<InT, MODE>(const RowArgs& a, int, hipStream_t s) {  \
+    return launch_rounds<InT, MODE, 4>(a, s);                               \
+  }
+
+}  // namespace rows
+}  // namespace orbit

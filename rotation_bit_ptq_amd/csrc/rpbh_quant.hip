@@ -1,0 +1,79 @@
+// Host entry of the row kernels (rotate, rotate + quantize, int8 pack): fills
+// the kernel arguments and dispatches on input type and mode.  The kernels
+// are in rpbh_impl.h, instantiated in the rpbh_*.hip files.
+#include "rpbh_impl.h"
+
+namespace orbit {
+
+hipError_t launch_rows(const RowJob& job, hipStream_t stream) {
+  using namespace rows;
+  RowArgs a = {};
+  a.d = job.d;
+  a.h = job.h;
+  a.log2h = 0;
+  while ((1 << a.log2h) < job.h) ++a.log2h;
+  a.nslots = job.d / kSlot;
+  a.nrounds = (a.nslots + kWave - 1) / kWave;
+  a.rows = job.rows;
+  a.perm = job.perm;
+  a.sign_bits = job.sign_bits;
+  a.in = job.in;
+  a.sqrt_d_over_h = (float)sqrt((double)job.d / job.h);
+  a.inv_sqrt_h = (float)(1.0 / sqrt((double)job.h));
+  a.inv_h = (float)(1.0 / job.h);
+  a.eps = job.eps;
+  a.ga = job.grid.a;
+  a.gb = job.grid.b;
+  a.cells = job.grid.cells;
+  a.nthr = job.grid.nthr;
+  a.grid_bias = 0xA8000000u;
+  for (int i = 0; i < job.grid.nthr && job.thresholds; ++i) a.thr[i] = job.thresholds[i];
+  a.idx_out = job.idx_out;
+  a.s_out = job.norm_f32_out;
+  a.r_out = job.norm_bf16_out;
+  a.xrot_f32 = job.xrot_f32_out;
+  a.xrot_f16 = (uint16_t*)job.rot_out;
+  a.group = job.group;
+  a.q_out = job.q_out;
+  a.scale_out = job.scale_out;
+  const bool quant = job.mode == RowMode::kActQuant || job.mode == RowMode::kWeightQuant;
+  a.grid_bytes = quant ? job.grid.cells * (int)sizeof(GridCell) : 0;
+  const int esz = job.in_dtype == ORBIT_BF16 ? 2 : 4;
+  a.row_bytes = 2 * job.d * esz;
+  a.wave_bytes = a.row_bytes;
+  if (job.rows == 0) return hipSuccess;
+  const bool bf16 = job.in_dtype == ORBIT_BF16;
+  // bf16 rows with h = 64, 128 or 256: transposed-gather kernels
+  const bool fast = bf16 && quant && job.bits != 1 && (job.h == 64 || job.h == 128 || job.h == 256);
+  if (fast) {
+    const int lt = job.h == 64 ? 2 : (job.h == 128 ? 3 : 4);
+    if (job.mode == RowMode::kActQuant) {
+      if (lt == 2) return launch_fast<kAct, 2>(a, job.bits, stream);
+      if (lt == 3) return launch_fast<kAct, 3>(a, job.bits, stream);
+      return launch_fast<kAct, 4>(a, job.bits, stream);
+    }
+    if (lt == 2) return launch_fast<kWeight, 2>(a, job.bits, stream);
+    if (lt == 3) return launch_fast<kWeight, 3>(a, job.bits, stream);
+    return launch_fast<kWeight, 4>(a, job.bits, stream);
+  }
+  switch (job.mode) {
+    case RowMode::kActQuant:
+      return bf16 ? launch_mode<uint16_t, kAct>(a, job.bits, stream)
+                  : launch_mode<float, kAct>(a, job.bits, stream);
+    case RowMode::kWeightQuant:
+      return bf16 ? launch_mode<uint16_t, kWeight>(a, job.bits, stream)
+                  : launch_mode<float, kWeight>(a, job.bits, stream);
+    case RowMode::kRotate:
+      if (job.out_dtype == ORBIT_F16)
+        return bf16 ? launch_mode<uint16_t, kRotF16>(a, 0, stream)
+                    : launch_mode<float, kRotF16>(a, 0, stream);
+      return bf16 ? launch_mode<uint16_t, kRotF32>(a, 0, stream)
+                  : launch_mode<float, kRotF32>(a, 0, stream);
+    case RowMode::kInt8Pack:
+      return bf16 ? launch_mode<uint16_t, kInt8>(a, 0, stream)
+                  : launch_mode<float, kInt8>(a, 0, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace orbit

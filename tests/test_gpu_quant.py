@@ -1,0 +1,145 @@
+"""GPU parity of the fused rotate + quantize kernels against the oracle.
+
+Checks (OrbitQuant page, Method): x' = Pi x within 1e-5 relative per token,
+s = ||x'|| within 1e-6, codebook indices bit-exact except where the rotated
+coordinate lies within 1e-6 of a decision threshold (fraction < 1e-5), and
+stored bf16 row norms bit-exact except within 1e-6 of a bf16 rounding tie.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity import as_f64, bits_of, check_indices, to_dev
+
+pytestmark = pytest.mark.gpu
+
+EPS = synth.EPS
+
+
+def _run_act(rbp, X, perm, signs, h, bits, label):
+    d = X.shape[1]
+    rot = rbp.Rotation(perm, signs, h)
+    cb = rbp.Codebook(d, bits)
+    ref_cb = oracle.codebook(bits)
+    idx, s, xr = rbp.quant_act(rot, cb, to_dev(X), EPS, debug_xrot=True)
+    torch.cuda.synchronize()
+    ref = oracle.quant_act(as_f64(X), perm, signs, h, ref_cb, bits, EPS)
+    xr = xr.cpu().numpy().astype(np.float64)
+    num = np.linalg.norm(xr - ref["xrot"], axis=1)
+    den = np.maximum(np.linalg.norm(ref["xrot"], axis=1), 1e-300)
+    assert np.all(num / den <= 1e-5), f"{label}: x' error {np.max(num / den)}"
+    s = s.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(s - ref["s"]) <= 1e-6 * ref["s"]), f"{label}: s"
+    stats, got = check_indices(idx, bits, d, ref["u"], ref_cb["thresholds"], label)
+    return stats
+
+
+CASES = [  # (label, workload, rows, bits)
+    ("tiny-f32-h64-a4", 1, 64, 4),
+    ("image-h128-a4", 2, 333, 4),
+    ("mlp-up-h256-a4", 4, 200, 4),
+    ("video-h128-a6", 5, 300, 6),
+]
+
+
+@pytest.mark.parametrize("label,cfg,rows,bits", CASES, ids=[c[0] for c in CASES])
+def test_quant_act_workloads(gpu_lib, label, cfg, rows, bits):
+    inp = synth.make(cfg, M=rows, N=8)
+    _run_act(gpu_lib, inp["X"], inp["perm"], inp["signs"], inp["h"], bits, label)
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 8])
+def test_quant_act_other_widths(gpu_lib, bits):
+    inp = synth.make(2, M=96, N=8)
+    _run_act(gpu_lib, inp["X"], inp["perm"], inp["signs"], inp["h"], bits, f"a{bits}")
+
+
+def test_quant_act_long_rows_two_pass(gpu_lib):
+    # d = 12288 (the MLP down projection input, 48 blocks of 256): rows longer
+    # than 4096 take the two-pass path
+    inp = synth.make(4, M=8)
+    g = np.random.default_rng(5)
+    X = synth.f32_to_bf16_bits(g.standard_normal((40, 12288)).astype(np.float32))
+    _run_act(gpu_lib, X, inp["perm2"], inp["signs2"], 256, 4, "down-d12288")
+
+
+@pytest.mark.parametrize("d,h", [(1040, 16), (48, 16), (3072, 32), (3072, 1024), (1024, 1024)])
+def test_quant_act_shapes(gpu_lib, d, h):
+    perm, signs = synth.rotation_params(d, 100 + d + h)
+    g = np.random.default_rng(d + h)
+    X = synth.f32_to_bf16_bits(g.standard_normal((70, d)).astype(np.float32))
+    _run_act(gpu_lib, X, perm, signs, h, 4, f"d{d}-h{h}")
+
+
+def test_block_rht_identity_permutation(gpu_lib):
+    # Block-RHT (the ablation's variant without the permutation)
+    d = 3072
+    _, signs = synth.rotation_params(d, 9)
+    inp = synth.make(2, M=64, N=8)
+    _run_act(gpu_lib, inp["X"], np.arange(d, dtype=np.int32), signs, 128, 4, "block-rht")
+
+
+def test_zero_and_nan_tokens(gpu_lib):
+    rbp = gpu_lib
+    inp = synth.make(2, M=8, N=8)
+    X = inp["X"].copy()
+    X[2] = 0                      # an all-zero token
+    X[5, 17] = 0x7FC0             # a NaN coordinate
+    rot = rbp.Rotation(inp["perm"], inp["signs"], inp["h"])
+    cb = rbp.Codebook(3072, 4)
+    idx, s = rbp.quant_act(rot, cb, to_dev(X), EPS)
+    s = s.cpu().numpy()
+    assert s[2] == 0.0 and np.isnan(s[5]) and np.all(np.isfinite(np.delete(s, 5)))
+    zero_codes = oracle.unpack_indices(idx[2:3].cpu().numpy(), 4, 3072)
+    assert np.all(zero_codes == 7)            # u = 0 -> #{t_j < 0} = 7
+
+
+def test_weight_pack_workloads(gpu_lib):
+    rbp = gpu_lib
+    for label, cfg, rows, bits, key in [("tiny-f32", 1, 256, 4, "W"), ("image", 2, 200, 4, "W"),
+                                        ("mlp-up-w2", 4, 150, 2, "W"), ("video", 5, 130, 4, "W")]:
+        inp = synth.make(cfg, M=8, N=rows)
+        W = inp[key].copy()
+        W[3] = 0                                     # a zero row: r = 0, u = 0
+        d = W.shape[1]
+        rot = rbp.Rotation(inp["perm"], inp["signs"], inp["h"])
+        cb = rbp.Codebook(d, bits)
+        ref_cb = oracle.codebook(bits)
+        idx, r = rbp.pack_weights(rot, cb, to_dev(W))
+        torch.cuda.synchronize()
+        ref = oracle.pack_weights(as_f64(W), inp["perm"], inp["signs"], inp["h"], ref_cb, bits)
+        check_indices(idx, bits, d, ref["u"], ref_cb["thresholds"], label)
+        got_r = bits_of(r)
+        bad = got_r != ref["r_bf16"]
+        if bad.any():
+            # only where the norm sits on a bf16 rounding tie (within 1e-6)
+            r64 = ref["r"][bad]
+            lo = oracle.bf16_bits_to_f64(oracle.f64_to_bf16_bits(r64 * (1 - 1e-6)))
+            hi = oracle.bf16_bits_to_f64(oracle.f64_to_bf16_bits(r64 * (1 + 1e-6)))
+            assert np.all(lo != hi), f"{label}: r mismatch off a tie"
+        assert got_r[3] == 0
+
+
+def test_weight_pack_long_rows(gpu_lib):
+    rbp = gpu_lib
+    inp = synth.make(4, M=8)
+    W = inp["W2"][:48]                           # down projection rows, d = 12288
+    rot = rbp.Rotation(inp["perm2"], inp["signs2"], 256)
+    cb = rbp.Codebook(12288, 2)
+    idx, r = rbp.pack_weights(rot, cb, to_dev(W))
+    ref_cb = oracle.codebook(2)
+    ref = oracle.pack_weights(as_f64(W), inp["perm2"], inp["signs2"], 256, ref_cb, 2)
+    check_indices(idx, 2, 12288, ref["u"], ref_cb["thresholds"], "down-w2")
+
+
+def test_deterministic(gpu_lib):
+    rbp = gpu_lib
+    inp = synth.make(2, M=256, N=8)
+    rot = rbp.Rotation(inp["perm"], inp["signs"], inp["h"])
+    cb = rbp.Codebook(3072, 4)
+    X = to_dev(inp["X"])
+    a = rbp.quant_act(rot, cb, X, EPS)
+    b = rbp.quant_act(rot, cb, X, EPS)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
