@@ -20,7 +20,7 @@
 //     [g KC/2, (g+1) KC/2), and sub-step s feeds k = g KC/2 + 8 s + 0..7.
 //     Both operands use the same assignment, so every dot product is the
 //     exact sum over all k while each lane reads one contiguous run of
-//     packed codes per row per chunk (32 bytes for 4-bit codes);
+//     packed codes per row per chunk (16 bytes for 4-bit codes);
 //   * codes go straight from global memory to registers (the next chunk is
 //     in flight while the current one is multiplied) and are decoded with
 //     an LDS table replicated per lane: a code byte and the lane number form
@@ -41,6 +41,7 @@ namespace qgemm {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x3 __attribute__((ext_vector_type(3)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 struct GemmArgs {
@@ -60,6 +61,7 @@ struct GemmArgs {
   int tiles_m, tiles_n;
   int table_a_offset;  // LDS byte offset of the activation codebook table
   int table_b_offset;  // LDS byte offset of the weight codebook table
+  int factor_offset;   // LDS byte offset of the tile's output factors
   uint16_t cent_a[256];
   uint16_t cent_b[256];
 };
@@ -77,29 +79,33 @@ __device__ __forceinline__ u32x2 lds_u32x2(uint32_t a) { return *(lds_u32x2_t*)(
 // Each operand type knows its chunk (kChunkK), how many bytes a lane loads
 // per chunk for one 32-row block, and how to turn sub-step s into a half8.
 
-template <int BITS>
+template <int BITS, int KC>
 struct CodeOp {  // packed b-bit codebook indices, LSB-first
   static constexpr int kBits = BITS;
-  static constexpr int kChunkK = 128;                 // 8 sub-steps of k = 16
-  static constexpr int kBytes = 8 * BITS;              // 64 codes per lane per chunk
+  static constexpr int kChunkK = KC;                   // KC / 16 sub-steps of k = 16
+  static constexpr int kBytes = KC * BITS / 16;        // KC / 2 codes per lane per chunk
   static constexpr int kDwords = kBytes / 4;
   static constexpr int kTableBytes = (BITS == 4 || BITS == 2 || BITS == 8) ? 65536 : 16384;
+  // LDS reads per sub-step (8 codes): 2-bit bytes give four values, 4-bit
+  // bytes and 3-bit pairs two, 6- and 8-bit codes one
+  static constexpr int kLookups = BITS == 2 ? 2 : (BITS == 4 || BITS == 3) ? 4 : 8;
   uint32_t w[kDwords];
 
   __device__ __forceinline__ void load(const uint8_t* p) {
-    if constexpr (kBytes % 16 == 0) {
+    int q = 0;
 #pragma unroll
-      for (int q = 0; q < kBytes / 16; ++q) {
-        const u32x4 v = *(const u32x4*)(p + 16 * q);
-        w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
-      }
-    } else {
-      static_assert(kBytes % 8 == 0, "unsupported width");
-#pragma unroll
-      for (int q = 0; q < kBytes / 8; ++q) {
-        const u32x2 v = *(const u32x2*)(p + 8 * q);
-        w[2 * q] = v.x; w[2 * q + 1] = v.y;
-      }
+    for (; q + 4 <= kDwords; q += 4) {
+      const u32x4 v = *(const u32x4*)(p + 4 * q);
+      w[q] = v.x; w[q + 1] = v.y; w[q + 2] = v.z; w[q + 3] = v.w;
+    }
+    if constexpr (kDwords % 4 == 3) {
+      const u32x3 v = *(const u32x3*)(p + 4 * q);
+      w[q] = v.x; w[q + 1] = v.y; w[q + 2] = v.z;
+    } else if constexpr (kDwords % 4 == 2) {
+      const u32x2 v = *(const u32x2*)(p + 4 * q);
+      w[q] = v.x; w[q + 1] = v.y;
+    } else if constexpr (kDwords % 4 == 1) {
+      w[q] = *(const uint32_t*)(p + 4 * q);
     }
   }
 
@@ -110,47 +116,41 @@ struct CodeOp {  // packed b-bit codebook indices, LSB-first
     return n == 32 ? v : (v & ((1u << n) - 1u));
   }
 
-  // `lb` is the lane's base in the decode table (see lane_base); every
-  // table address is formed in one v_perm or v_lshl_or and read straight
-  // from LDS.
-  __device__ __forceinline__ half8 decode(int s, uint32_t lb) const {
-    uint32_t o[4];
+  // LDS address of lookup l of sub-step s.  `lb` is the lane's base in the
+  // decode table (see lane_base); the address takes one v_perm (or a
+  // bit-field extract and a shift-or) and no other arithmetic.
+  __device__ __forceinline__ uint32_t addr(int s, int l, uint32_t lb) const {
     if constexpr (BITS == 4) {
       // table [byte][64 lanes] of fp16 pairs: addr = base | byte << 8 | lane << 2
-      const uint32_t x = w[s];
-      o[0] = lds_u32(__builtin_amdgcn_perm(x, lb, 0x0c020400u));
-      o[1] = lds_u32(__builtin_amdgcn_perm(x, lb, 0x0c020500u));
-      o[2] = lds_u32(__builtin_amdgcn_perm(x, lb, 0x0c020600u));
-      o[3] = lds_u32(__builtin_amdgcn_perm(x, lb, 0x0c020700u));
+      return __builtin_amdgcn_perm(w[s], lb, 0x0c020400u + ((uint32_t)l << 8));
     } else if constexpr (BITS == 2) {
       // table [byte][32 lanes] of fp16 quads: addr = base | byte << 8 | (lane & 31) << 3
-      const uint32_t x = w[s >> 1];
-      const uint32_t sel0 = (s & 1) ? 0x0c020600u : 0x0c020400u;
-      const uint32_t sel1 = (s & 1) ? 0x0c020700u : 0x0c020500u;
-      const u32x2 q0 = lds_u32x2(__builtin_amdgcn_perm(x, lb, sel0));
-      const u32x2 q1 = lds_u32x2(__builtin_amdgcn_perm(x, lb, sel1));
-      o[0] = q0.x; o[1] = q0.y; o[2] = q1.x; o[3] = q1.y;
+      return __builtin_amdgcn_perm(w[s >> 1], lb, 0x0c020400u + ((uint32_t)(2 * (s & 1) + l) << 8));
     } else if constexpr (BITS == 8) {
       // table [byte][64 lanes], fp16 in the low half of each entry
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t x = w[2 * s + (j >> 1)];
-        const uint32_t s0 = (j & 1) ? 0x0c020600u : 0x0c020400u;
-        const uint32_t s1 = (j & 1) ? 0x0c020700u : 0x0c020500u;
-        o[j] = lds_u16(__builtin_amdgcn_perm(x, lb, s0)) | (lds_u16(__builtin_amdgcn_perm(x, lb, s1)) << 16);
-      }
+      return __builtin_amdgcn_perm(w[2 * s + (l >> 2)], lb, 0x0c020400u + ((uint32_t)(l & 3) << 8));
     } else if constexpr (BITS == 6) {
       // table [index][64 lanes], fp16 in the low half of each entry
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t i0 = field(48 * s + 12 * j, 6), i1 = field(48 * s + 12 * j + 6, 6);
-        o[j] = lds_u16((i0 << 8) | lb) | (lds_u16((i1 << 8) | lb) << 16);
-      }
+      return (field(48 * s + 6 * l, 6) << 8) | lb;
     } else {
       static_assert(BITS == 3, "unsupported width");
       // table [pair of 3-bit indices][64 lanes] of fp16 pairs
+      return (field(24 * s + 6 * l, 6) << 8) | lb;
+    }
+  }
+
+  // the sub-step's eight fp16 values from the addresses of its lookups
+  static __device__ __forceinline__ half8 gather(const uint32_t (&a)[kLookups]) {
+    uint32_t o[4];
+    if constexpr (BITS == 2) {
+      const u32x2 q0 = lds_u32x2(a[0]), q1 = lds_u32x2(a[1]);
+      o[0] = q0.x; o[1] = q0.y; o[2] = q1.x; o[3] = q1.y;
+    } else if constexpr (kLookups == 4) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) o[j] = lds_u32((field(24 * s + 6 * j, 6) << 8) | lb);
+      for (int j = 0; j < 4; ++j) o[j] = lds_u32(a[j]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = lds_u16(a[2 * j]) | (lds_u16(a[2 * j + 1]) << 16);
     }
     return __builtin_bit_cast(half8, make_uint4(o[0], o[1], o[2], o[3]));
   }
@@ -163,31 +163,36 @@ struct CodeOp {  // packed b-bit codebook indices, LSB-first
   }
 };
 
-// Builds the lane-replicated decode table of a codebook in LDS.
+// Chunk length of a pair of code widths: 128 k while the raw codes of both
+// operands fit the register budget (2- and 4-bit codes), else 64.
+template <int BA, int BB>
+struct CodeChunk {
+  static constexpr int kK = ((BA == 2 || BA == 4) && (BB == 2 || BB == 4)) ? 128 : 64;
+};
+
+// Builds the lane-replicated decode table of a codebook in LDS (256 threads).
+// Every table row is 256 bytes (one entry per lane, or per lane pair for the
+// 2-bit quads); thread t writes 16-byte piece t % 16 of rows t / 16 + 16 k.
 template <int BITS>
-__device__ void build_table(char* tab, const uint16_t* cent) {
-  if constexpr (BITS == 4) {
-    for (int e = threadIdx.x; e < 256 * 64; e += blockDim.x) {
-      const int byte = e >> 6;
-      ((uint32_t*)tab)[e] = (uint32_t)cent[byte & 15] | ((uint32_t)cent[byte >> 4] << 16);
+__device__ __forceinline__ void build_table(char* tab, const uint16_t* cent) {
+  constexpr int kRows = (BITS == 6 || BITS == 3) ? 64 : 256;
+  const int q = threadIdx.x & 15, r0 = threadIdx.x >> 4;
+#pragma unroll
+  for (int k = 0; k < kRows / 16; ++k) {
+    const int r = r0 + 16 * k;
+    u32x4 v;
+    if constexpr (BITS == 2) {
+      const uint32_t lo = (uint32_t)cent[r & 3] | ((uint32_t)cent[(r >> 2) & 3] << 16);
+      const uint32_t hi = (uint32_t)cent[(r >> 4) & 3] | ((uint32_t)cent[r >> 6] << 16);
+      v = u32x4{lo, hi, lo, hi};
+    } else {
+      uint32_t e;
+      if constexpr (BITS == 4) e = (uint32_t)cent[r & 15] | ((uint32_t)cent[r >> 4] << 16);
+      else if constexpr (BITS == 3) e = (uint32_t)cent[r & 7] | ((uint32_t)cent[r >> 3] << 16);
+      else e = cent[r];  // 6- and 8-bit: fp16 in the low half
+      v = u32x4{e, e, e, e};
     }
-  } else if constexpr (BITS == 2) {
-    for (int e = threadIdx.x; e < 256 * 32; e += blockDim.x) {
-      const int byte = e >> 5;
-      uint2 q;
-      q.x = (uint32_t)cent[byte & 3] | ((uint32_t)cent[(byte >> 2) & 3] << 16);
-      q.y = (uint32_t)cent[(byte >> 4) & 3] | ((uint32_t)cent[byte >> 6] << 16);
-      ((uint2*)tab)[e] = q;
-    }
-  } else if constexpr (BITS == 8) {
-    for (int e = threadIdx.x; e < 256 * 64; e += blockDim.x) ((uint32_t*)tab)[e] = cent[e >> 6];
-  } else if constexpr (BITS == 6) {
-    for (int e = threadIdx.x; e < 64 * 64; e += blockDim.x) ((uint32_t*)tab)[e] = cent[e >> 6];
-  } else {
-    for (int e = threadIdx.x; e < 64 * 64; e += blockDim.x) {
-      const int pair = e >> 6;
-      ((uint32_t*)tab)[e] = (uint32_t)cent[pair & 7] | ((uint32_t)cent[pair >> 3] << 16);
-    }
+    *(u32x4*)(tab + r * 256 + q * 16) = v;
   }
 }
 
@@ -283,16 +288,39 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
   const int wave = threadIdx.x >> 6;
   const int wm = wave & 1, wn = wave >> 1;
 
+  int tm, tn;
+  tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
+
+  // The tile's output factors go to LDS next to the tables: s_m / K per
+  // token, r_n and the bias per weight row (1, 1 and the bias for the int8
+  // GEMM; zero past the end).  Their loads are issued before the tables are
+  // built so the two overlap.
+  float* const fs = (float*)(smem + g.factor_offset);
+  float* const fr = fs + TM;
+  float* const fb = fr + TN;
+  const int t = threadIdx.x;
+  float vs = 1.0f, vr = 1.0f, vb = 0.0f;
+  {
+    const long long m = (long long)tm * TM + t, n = (long long)tn * TN + t;
+    if (KIND == 0 && t < TM) vs = m < g.M ? g.s[m] * g.inv_k : 0.0f;
+    if (t < TN) {
+      if (KIND == 0) vr = n < g.N ? __uint_as_float((uint32_t)g.r_bf16[n] << 16) : 0.0f;
+      vb = n < g.N ? load_bias(g, n) : 0.0f;
+    }
+  }
   if constexpr (KIND == 0) {
     build_table<OpA::kBits>(smem + g.table_a_offset, g.cent_a);
     if (g.table_a_offset != g.table_b_offset) build_table<OpB::kBits>(smem + g.table_b_offset, g.cent_b);
-    __syncthreads();
   }
+  if (t < TM) fs[t] = vs;
+  if (t < TN) {
+    fr[t] = vr;
+    fb[t] = vb;
+  }
+  __syncthreads();
   const uint32_t lb_a = OpA::lane_base((uint32_t)g.table_a_offset, lane);
   const uint32_t lb_b = OpB::lane_base((uint32_t)g.table_b_offset, lane);
 
-  int tm, tn;
-  tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
   const long long m_base = (long long)tm * TM + wm * (TM / 2);
   const long long n_base = (long long)tn * TN + wn * (TN / 2);
   const int r32 = lane & 31, half = lane >> 5;
@@ -324,154 +352,194 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[j][i][q] = 0.0f;
 
-  // Raw codes of chunk c + 1 load into the other of two buffers while chunk
-  // c is decoded and multiplied.  Decoded token operands are single-
-  // buffered: block i is re-decoded for the next sub-step right after its
-  // last MFMA of this one; decoded weight operands alternate between two
-  // sets, the next set decoded at the start of a sub-step.
-  OpA ra0[WM], ra1[WM];
-  OpB rb0[WN], rb1[WN];
-  auto load_chunk = [&](int c, OpA (&xa)[WM], OpB (&xb)[WN]) {
+  const int nchunks = (int)(g.K / KC);  // >= 1
+  if constexpr (KIND == 0) {
+    // Software pipeline over the sub-steps t of the K loop.  Sub-step t runs
+    // its MFMAs on operands gathered during t - 1, gathers the operands of
+    // t + 1 from LDS with addresses formed during t - 1, and forms the
+    // addresses of t + 2 from the raw codes, so no instruction waits on a
+    // result produced just before it.  Raw codes sit in two buffers: chunk
+    // c + 2 is loaded into chunk c's buffer as soon as chunk c's last
+    // addresses are formed (two sub-steps before its end), a full chunk
+    // before it is first read.  Loads past the last chunk re-read the last
+    // chunk, and gathers and addresses past the end read valid table
+    // entries; neither touches the accumulators.
+    OpA ra[2][WM];
+    OpB rb[2][WN];
+    uint32_t adr_a[WM][OpA::kLookups], adr_b[WN][OpB::kLookups];
+    half8 va[2][WM], vb[2][WN];
+    const int last = nchunks - 1;
+    auto load = [&](int p, int c) {
+      c = c < last ? c : last;
 #pragma unroll
-    for (int i = 0; i < WM; ++i) xa[i].load(g.a + oa[i] + (uint32_t)c * kChunkA);
+      for (int i = 0; i < WM; ++i) ra[p][i].load(g.a + oa[i] + (uint32_t)c * kChunkA);
 #pragma unroll
-    for (int j = 0; j < WN; ++j) {
-      xb[j].load(g.b + ob[j] + (uint32_t)c * kChunkB);
-      if constexpr (KIND == 1) {
-        const uint32_t gi = (uint32_t)(c * KC) / 128u;  // group of 128 k
-        const uint32_t sc = g.scale_f16[nrow[j] * (uint32_t)g.groups_per_row + gi];
-        xb[j].scale2 = sc | (sc << 16);
+      for (int j = 0; j < WN; ++j) rb[p][j].load(g.b + ob[j] + (uint32_t)c * kChunkB);
+    };
+    auto form = [&](int p, int st) {
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int l = 0; l < OpA::kLookups; ++l) adr_a[i][l] = ra[p][i].addr(st, l, lb_a);
+#pragma unroll
+      for (int j = 0; j < WN; ++j)
+#pragma unroll
+        for (int l = 0; l < OpB::kLookups; ++l) adr_b[j][l] = rb[p][j].addr(st, l, lb_b);
+    };
+    auto gather = [&](int q) {
+#pragma unroll
+      for (int i = 0; i < WM; ++i) va[q][i] = OpA::gather(adr_a[i]);
+#pragma unroll
+      for (int j = 0; j < WN; ++j) vb[q][j] = OpB::gather(adr_b[j]);
+    };
+    auto mma = [&](int q) {
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j)
+          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vb[q][j], va[q][i], acc[j][i], 0, 0, 0);
+    };
+    auto chunk = [&](int p, int c) {
+#pragma unroll
+      for (int st = 0; st < STEPS; ++st) {
+        if (st == STEPS - 2) load(p, c + 2);
+        gather((st + 1) & 1);
+        if (st + 2 < STEPS) form(p, st + 2);
+        else form(p ^ 1, st + 2 - STEPS);
+        mma(st & 1);
+        __builtin_amdgcn_sched_barrier(0);
       }
+    };
+    load(0, 0);
+    load(1, 1);
+    form(0, 0);
+    gather(0);
+    form(0, 1);
+    int c = 0;
+    for (; c + 1 < nchunks; c += 2) {
+      chunk(0, c);
+      chunk(1, c + 1);
     }
-  };
-  half8 av[WM], bv0[WN], bv1[WN];
-  auto mfmas = [&](const half8 (&bcur)[WN], int i) {
-#pragma unroll
-    for (int j = 0; j < WN; ++j)
-      acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bcur[j], av[i], acc[j][i], 0, 0, 0);
-  };
-  // MFMAs of one sub-step with operands (bcur, av) while the next sub-step
-  // (xa, xb, ns) is decoded into (av, bnext)
-  auto substep_next = [&](const OpA (&xa)[WM], const OpB (&xb)[WN], int ns,
-                          const half8 (&bcur)[WN], half8 (&bnext)[WN]) {
-#pragma unroll
-    for (int j = 0; j < WN; ++j) bnext[j] = xb[j].decode(ns, lb_b);
-#pragma unroll
-    for (int i = 0; i < WM; ++i) {
-      mfmas(bcur, i);
-      av[i] = xa[i].decode(ns, lb_a);
-    }
-    // keep the scheduler from hoisting later sub-steps' decodes (and their
-    // registers) across this point
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  auto substep_last = [&](const half8 (&bcur)[WN]) {
-#pragma unroll
-    for (int i = 0; i < WM; ++i) mfmas(bcur, i);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  // the STEPS sub-steps of the chunk in (xa, xb); the last one decodes
-  // sub-step 0 of the chunk in (ya, yb)
-  auto chunk_next = [&](const OpA (&xa)[WM], const OpB (&xb)[WN], const OpA (&ya)[WM],
-                        const OpB (&yb)[WN]) {
-#pragma unroll
-    for (int s = 0; s < STEPS; s += 2) {
-      substep_next(xa, xb, s + 1, bv0, bv1);
-      if (s + 2 < STEPS) substep_next(xa, xb, s + 2, bv1, bv0);
-      else substep_next(ya, yb, 0, bv1, bv0);
-    }
-  };
-  auto chunk_last = [&](const OpA (&xa)[WM], const OpB (&xb)[WN]) {
-#pragma unroll
-    for (int s = 0; s < STEPS; s += 2) {
-      substep_next(xa, xb, s + 1, bv0, bv1);
-      if (s + 2 < STEPS) substep_next(xa, xb, s + 2, bv1, bv0);
-      else substep_last(bv1);
-    }
-  };
+    if (c < nchunks) chunk(0, c);
+  } else {
+    // Raw codes of chunk c + 1 load into the other of two buffers while chunk
+    // c is decoded and multiplied.  Decoded token operands are single-
+    // buffered: block i is re-decoded for the next sub-step right after its
+    // last MFMA of this one; decoded weight operands alternate between two
+    // sets, the next set decoded at the start of a sub-step.
+    OpA ra0[WM], ra1[WM];
+    OpB rb0[WN], rb1[WN];
+    auto load_chunk = [&](int c, OpA (&xa)[WM], OpB (&xb)[WN]) {
+  #pragma unroll
+      for (int i = 0; i < WM; ++i) xa[i].load(g.a + oa[i] + (uint32_t)c * kChunkA);
+  #pragma unroll
+      for (int j = 0; j < WN; ++j) {
+        xb[j].load(g.b + ob[j] + (uint32_t)c * kChunkB);
+        if constexpr (KIND == 1) {
+          const uint32_t gi = (uint32_t)(c * KC) / 128u;  // group of 128 k
+          const uint32_t sc = g.scale_f16[nrow[j] * (uint32_t)g.groups_per_row + gi];
+          xb[j].scale2 = sc | (sc << 16);
+        }
+      }
+    };
+    half8 av[WM], bv0[WN], bv1[WN];
+    auto mfmas = [&](const half8 (&bcur)[WN], int i) {
+  #pragma unroll
+      for (int j = 0; j < WN; ++j)
+        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bcur[j], av[i], acc[j][i], 0, 0, 0);
+    };
+    // MFMAs of one sub-step with operands (bcur, av) while the next sub-step
+    // (xa, xb, ns) is decoded into (av, bnext)
+    auto substep_next = [&](const OpA (&xa)[WM], const OpB (&xb)[WN], int ns,
+                            const half8 (&bcur)[WN], half8 (&bnext)[WN]) {
+  #pragma unroll
+      for (int j = 0; j < WN; ++j) bnext[j] = xb[j].decode(ns, lb_b);
+  #pragma unroll
+      for (int i = 0; i < WM; ++i) {
+        mfmas(bcur, i);
+        av[i] = xa[i].decode(ns, lb_a);
+      }
+      // keep the scheduler from hoisting later sub-steps' decodes (and their
+      // registers) across this point
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto substep_last = [&](const half8 (&bcur)[WN]) {
+  #pragma unroll
+      for (int i = 0; i < WM; ++i) mfmas(bcur, i);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // the STEPS sub-steps of the chunk in (xa, xb); the last one decodes
+    // sub-step 0 of the chunk in (ya, yb)
+    auto chunk_next = [&](const OpA (&xa)[WM], const OpB (&xb)[WN], const OpA (&ya)[WM],
+                          const OpB (&yb)[WN]) {
+  #pragma unroll
+      for (int s = 0; s < STEPS; s += 2) {
+        substep_next(xa, xb, s + 1, bv0, bv1);
+        if (s + 2 < STEPS) substep_next(xa, xb, s + 2, bv1, bv0);
+        else substep_next(ya, yb, 0, bv1, bv0);
+      }
+    };
+    auto chunk_last = [&](const OpA (&xa)[WM], const OpB (&xb)[WN]) {
+  #pragma unroll
+      for (int s = 0; s < STEPS; s += 2) {
+        substep_next(xa, xb, s + 1, bv0, bv1);
+        if (s + 2 < STEPS) substep_next(xa, xb, s + 2, bv1, bv0);
+        else substep_last(bv1);
+      }
+    };
 
-  // nchunks >= 1; the loop body always has a chunk after the one it works on
-  const int nchunks = (int)(g.K / KC);
-  load_chunk(0, ra0, rb0);
-#pragma unroll
-  for (int i = 0; i < WM; ++i) av[i] = ra0[i].decode(0, lb_a);
-#pragma unroll
-  for (int j = 0; j < WN; ++j) bv0[j] = rb0[j].decode(0, lb_b);
-  int c = 0;
-  for (; c + 2 < nchunks; c += 2) {
-    load_chunk(c + 1, ra1, rb1);
-    chunk_next(ra0, rb0, ra1, rb1);
-    load_chunk(c + 2, ra0, rb0);
-    chunk_next(ra1, rb1, ra0, rb0);
-  }
-  if (c + 1 < nchunks) {  // two chunks left
-    load_chunk(c + 1, ra1, rb1);
-    chunk_next(ra0, rb0, ra1, rb1);
-    chunk_last(ra1, rb1);
-  } else {                // one chunk left
-    chunk_last(ra0, rb0);
+    // the loop body always has a chunk after the one it works on
+    load_chunk(0, ra0, rb0);
+  #pragma unroll
+    for (int i = 0; i < WM; ++i) av[i] = ra0[i].decode(0, lb_a);
+  #pragma unroll
+    for (int j = 0; j < WN; ++j) bv0[j] = rb0[j].decode(0, lb_b);
+    int c = 0;
+    for (; c + 2 < nchunks; c += 2) {
+      load_chunk(c + 1, ra1, rb1);
+      chunk_next(ra0, rb0, ra1, rb1);
+      load_chunk(c + 2, ra0, rb0);
+      chunk_next(ra1, rb1, ra0, rb0);
+    }
+    if (c + 1 < nchunks) {  // two chunks left
+      load_chunk(c + 1, ra1, rb1);
+      chunk_next(ra0, rb0, ra1, rb1);
+      chunk_last(ra1, rb1);
+    } else {                // one chunk left
+      chunk_last(ra0, rb0);
+    }
   }
 
   // epilogue: block (j, i) of lane l holds weight rows
   // n_base + 32 j + 8 qq + 4 half + 0..3 (qq < 4) of token m_base + 32 i + r32.
-  // Per run of four weight rows the factors r_n and the bias are read once
-  // and applied to all WM token blocks.  A wave whose outputs lie inside the
-  // matrix, with row length and pointers aligned for 8/16-byte accesses,
-  // takes the vector path with no per-element checks.
+  // The factors come from LDS.  A wave whose outputs lie inside the matrix,
+  // with row length and output pointer aligned for 8/16-byte stores, takes
+  // the vector path with no per-element checks.
+  const float* const ws = fs + wm * (TM / 2) + r32;
+  const float* const wr = fr + wn * (TN / 2) + 4 * half;
+  const float* const wb = fb + wn * (TN / 2) + 4 * half;
   float sm[WM];
 #pragma unroll
-  for (int i = 0; i < WM; ++i) {
-    const long long m = m_base + 32 * i + r32;
-    sm[i] = (KIND == 0) ? g.s[m < g.M ? m : g.M - 1] * g.inv_k : 1.0f;
-  }
+  for (int i = 0; i < WM; ++i) sm[i] = ws[32 * i];
   const bool f32_out = g.out_dtype != ORBIT_BF16;
-  const uintptr_t align_bits = (uintptr_t)g.out | (uintptr_t)g.r_bf16 | (uintptr_t)g.bias;
-  const bool fast = (g.N & 3) == 0 && (align_bits & 15) == 0 && m_base + TM / 2 <= g.M &&
+  const bool fast = (g.N & 3) == 0 && ((uintptr_t)g.out & 15) == 0 && m_base + TM / 2 <= g.M &&
                     n_base + TN / 2 <= g.N;
-  // straight-line epilogue for one output type and bias kind (0 none,
-  // 1 bf16, 2 f32): every column factor is loaded first, then the outputs
-  // are scaled, rounded and stored four at a time
-  auto epi = [&](auto f32c, auto biasc) {
+  auto epi = [&](auto f32c) {
     constexpr bool F32 = decltype(f32c)::value;
-    constexpr int BK = decltype(biasc)::value;
-    u32x2 rb[WN][4];
-    float4 cb[WN][4];
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
         const long long n0 = n_base + 32 * j + 8 * qq + 4 * half;
-        if constexpr (KIND == 0) rb[j][qq] = *(const u32x2*)(g.r_bf16 + n0);
-        if constexpr (BK == 1) {
-          const u32x2 bb = *(const u32x2*)((const uint16_t*)g.bias + n0);
-          cb[j][qq] = make_float4(__uint_as_float(bb.x << 16), __uint_as_float(bb.x & 0xffff0000u),
-                                  __uint_as_float(bb.y << 16), __uint_as_float(bb.y & 0xffff0000u));
-        } else if constexpr (BK == 2) {
-          cb[j][qq] = *(const float4*)((const float*)g.bias + n0);
-        } else {
-          cb[j][qq] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        }
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < WN; ++j) {
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const long long n0 = n_base + 32 * j + 8 * qq + 4 * half;
-        float cf[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-        if constexpr (KIND == 0) {
-          cf[0] = __uint_as_float(rb[j][qq].x << 16);
-          cf[1] = __uint_as_float(rb[j][qq].x & 0xffff0000u);
-          cf[2] = __uint_as_float(rb[j][qq].y << 16);
-          cf[3] = __uint_as_float(rb[j][qq].y & 0xffff0000u);
-        }
-        const float cbv[4] = {cb[j][qq].x, cb[j][qq].y, cb[j][qq].z, cb[j][qq].w};
+        const float4 cf = *(const float4*)(wr + 32 * j + 8 * qq);
+        const float4 cb = *(const float4*)(wb + 32 * j + 8 * qq);
+        const float cfv[4] = {cf.x, cf.y, cf.z, cf.w}, cbv[4] = {cb.x, cb.y, cb.z, cb.w};
 #pragma unroll
         for (int i = 0; i < WM; ++i) {
           const long long m = m_base + 32 * i + r32;
           float y[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) y[q] = __builtin_fmaf(acc[j][i][4 * qq + q], sm[i] * cf[q], cbv[q]);
+          for (int q = 0; q < 4; ++q) y[q] = __builtin_fmaf(acc[j][i][4 * qq + q], sm[i] * cfv[q], cbv[q]);
           if constexpr (F32) {
             *(float4*)((float*)g.out + m * g.N + n0) = make_float4(y[0], y[1], y[2], y[3]);
           } else {
@@ -485,18 +553,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
     }
   };
   if (fast) {
-    using T = std::true_type;
-    using F = std::false_type;
-    const int bk = !g.bias ? 0 : (g.bias_dtype == ORBIT_BF16 ? 1 : 2);
-    if (f32_out) {
-      if (bk == 0) epi(T{}, std::integral_constant<int, 0>{});
-      else if (bk == 1) epi(T{}, std::integral_constant<int, 1>{});
-      else epi(T{}, std::integral_constant<int, 2>{});
-    } else {
-      if (bk == 0) epi(F{}, std::integral_constant<int, 0>{});
-      else if (bk == 1) epi(F{}, std::integral_constant<int, 1>{});
-      else epi(F{}, std::integral_constant<int, 2>{});
-    }
+    if (f32_out) epi(std::true_type{});
+    else epi(std::false_type{});
     return;
   }
 #pragma unroll
@@ -507,8 +565,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
       for (int q = 0; q < 4; ++q) {
         const long long n = n_base + 32 * j + 8 * qq + 4 * half + q;
         if (n >= g.N) continue;
-        const float cf = (KIND == 0) ? __uint_as_float((uint32_t)g.r_bf16[n] << 16) : 1.0f;
-        const float cb = load_bias(g, n);
+        const float cf = wr[32 * j + 8 * qq + q], cb = wb[32 * j + 8 * qq + q];
 #pragma unroll
         for (int i = 0; i < WM; ++i) {
           const long long m = m_base + 32 * i + r32;
@@ -530,6 +587,8 @@ hipError_t launch_tile(GemmArgs& g, int lds, hipStream_t stream) {
   const long long tiles = (long long)g.tiles_m * g.tiles_n;
   if (tiles == 0) return hipSuccess;
   if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
+  g.factor_offset = lds;  // after the tables (a multiple of 16 KB, or 0)
+  lds += (TM + 2 * TN) * (int)sizeof(float);
   auto kern = gemm_kernel<KIND, OpA, OpB, WM, WN>;
   static LaunchCache cache;
   hipError_t e = prepare_launch(cache, (const void*)kern, 256, lds, nullptr);
@@ -539,11 +598,20 @@ hipError_t launch_tile(GemmArgs& g, int lds, hipStream_t stream) {
 }
 
 // Picks the tile: large tiles when there are enough of them to fill the
-// 256 compute units, smaller ones otherwise.
+// 256 compute units, smaller ones otherwise.  Codes wider than 4 bits (and
+// 3-bit codes) hold more raw bits and table addresses per operand, so their
+// widest wave tile is 4 x 2 blocks instead of 4 x 3, and 2 x 2 for the
+// pairs whose registers do not fit 4 x 2 (both operands 6- or 8-bit, or
+// 8-bit tokens with 3-bit weights).
 template <int KIND, class OpA, class OpB>
 hipError_t launch_shape(GemmArgs& g, int lds, hipStream_t stream) {
   auto tiles = [&](int tm, int tn) { return ((g.M + tm - 1) / tm) * ((g.N + tn - 1) / tn); };
-  if (tiles(256, 192) >= 192) return launch_tile<KIND, OpA, OpB, 4, 3>(g, lds, stream);
+  constexpr bool kNarrow = KIND == 1 || OpA::kChunkK == 128;
+  if constexpr (kNarrow) {
+    if (tiles(256, 192) >= 192) return launch_tile<KIND, OpA, OpB, 4, 3>(g, lds, stream);
+  } else if constexpr (!(OpA::kLookups + OpB::kLookups >= 16 || (OpA::kBits == 8 && OpB::kBits == 3))) {
+    if (tiles(256, 128) >= 192) return launch_tile<KIND, OpA, OpB, 4, 2>(g, lds, stream);
+  }
   if (tiles(128, 128) >= 128) return launch_tile<KIND, OpA, OpB, 2, 2>(g, lds, stream);
   return launch_tile<KIND, OpA, OpB, 1, 1>(g, lds, stream);
 }
@@ -554,7 +622,10 @@ hipError_t launch_shape(GemmArgs& g, int lds, hipStream_t stream) {
 // alignment.  A shared codebook uses one table.
 template <int BA, int BB>
 hipError_t launch_codes(GemmArgs& g, hipStream_t stream, bool same_table) {
-  const int tab_a = CodeOp<BA>::kTableBytes, tab_b = CodeOp<BB>::kTableBytes;
+  constexpr int KC = CodeChunk<BA, BB>::kK;
+  using OpA = CodeOp<BA, KC>;
+  using OpB = CodeOp<BB, KC>;
+  const int tab_a = OpA::kTableBytes, tab_b = OpB::kTableBytes;
   int lds;
   if (same_table) {
     g.table_a_offset = 0;
@@ -569,7 +640,7 @@ hipError_t launch_codes(GemmArgs& g, hipStream_t stream, bool same_table) {
     g.table_a_offset = tab_b;
     lds = tab_a + tab_b;
   }
-  return launch_shape<0, CodeOp<BA>, CodeOp<BB>>(g, lds, stream);
+  return launch_shape<0, OpA, OpB>(g, lds, stream);
 }
 
 // Defined (and instantiated) in qgemm_a<BA>.hip, one translation unit per
