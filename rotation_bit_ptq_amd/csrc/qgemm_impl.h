@@ -32,6 +32,7 @@
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "orbit_internal.h"
 
@@ -89,6 +90,12 @@ struct CodeOp {  // packed b-bit codebook indices, LSB-first
   // LDS reads per sub-step (8 codes): 2-bit bytes give four values, 4-bit
   // bytes and 3-bit pairs two, 6- and 8-bit codes one
   static constexpr int kLookups = BITS == 2 ? 2 : (BITS == 4 || BITS == 3) ? 4 : 8;
+  // instruction counts per operand and sub-step, for the issue schedule:
+  // LDS reads of a gather, VALU work of forming addresses (and of joining
+  // 16-bit entries), and global loads per chunk
+  static constexpr int kReads = kLookups;
+  static constexpr int kValu = (BITS == 2 || BITS == 4) ? kLookups : (BITS == 8 ? 12 : 3 * kLookups);
+  static constexpr int kLoads = (kDwords + 3) / 4;
   uint32_t w[kDwords];
 
   __device__ __forceinline__ void load(const uint8_t* p) {
@@ -275,6 +282,24 @@ __device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int& tm
   tn = r / gsize;
 }
 
+// Issue schedule of one sub-step: NMF MFMAs, each followed by its share of
+// the NDS LDS reads, NVA VALU instructions and NVM global loads, so the
+// matrix pipe is handed a new MFMA while the previous one is still running.
+template <int NMF, int NDS, int NVA, int NVM, int K>
+__device__ __forceinline__ void issue_slot() {
+  constexpr int ds = NDS * (K + 1) / NMF - NDS * K / NMF;
+  constexpr int va = NVA * (K + 1) / NMF - NVA * K / NMF;
+  constexpr int vm = NVM * (K + 1) / NMF - NVM * K / NMF;
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+  if constexpr (vm > 0) __builtin_amdgcn_sched_group_barrier(0x020, vm, 0);  // VMEM read
+  if constexpr (ds > 0) __builtin_amdgcn_sched_group_barrier(0x100, ds, 0);  // DS read
+  if constexpr (va > 0) __builtin_amdgcn_sched_group_barrier(0x002, va, 0);  // VALU
+}
+template <int NMF, int NDS, int NVA, int NVM, int... K>
+__device__ __forceinline__ void issue_schedule(std::integer_sequence<int, K...>) {
+  (issue_slot<NMF, NDS, NVA, NVM, K>(), ...);
+}
+
 // KIND 0: codebook x codebook; KIND 1: fp16 x int8 with group scales.
 // WM token blocks and WN weight blocks of 32 per wave.
 template <int KIND, class OpA, class OpB, int WM, int WN>
@@ -399,14 +424,27 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
         for (int j = 0; j < WN; ++j)
           acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vb[q][j], va[q][i], acc[j][i], 0, 0, 0);
     };
+    constexpr int NMF = WM * WN;
+    constexpr int NDS = WM * OpA::kReads + WN * OpB::kReads;
+    constexpr int NVA = WM * OpA::kValu + WN * OpB::kValu;
+    constexpr int NVM = WM * OpA::kLoads + WN * OpB::kLoads;
+    using Slots = std::make_integer_sequence<int, NMF>;
+    // Each sub-step starts by waiting for all LDS reads issued so far: they
+    // are the previous sub-step's gathers, long complete, and one full wait
+    // here keeps the MFMAs below free of partial waits (the LDS counter only
+    // reaches 15, so a partial wait behind this sub-step's own gathers would
+    // stall on them).
     auto chunk = [&](int p, int c) {
 #pragma unroll
       for (int st = 0; st < STEPS; ++st) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt/expcnt untouched
         if (st == STEPS - 2) load(p, c + 2);
         gather((st + 1) & 1);
         if (st + 2 < STEPS) form(p, st + 2);
         else form(p ^ 1, st + 2 - STEPS);
         mma(st & 1);
+        if (st == STEPS - 2) issue_schedule<NMF, NDS, NVA, NVM>(Slots{});
+        else issue_schedule<NMF, NDS, NVA, 0>(Slots{});
         __builtin_amdgcn_sched_barrier(0);
       }
     };
