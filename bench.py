@@ -41,7 +41,14 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(HERE, "profiles", "traffic.json"),
                     help="per-launch HBM bytes measured with rocprofv3 counters")
+    ap.add_argument("--only", choices=["quant", "gemm", "copy"], default=None,
+                    help="launch only one kernel --steps times (for counter runs): the "
+                         "activation rotate+quantize, the decode GEMM, or a plain device "
+                         "copy of COPY_BYTES that calibrates FETCH_SIZE / WRITE_SIZE")
     return ap.parse_args()
+
+
+COPY_BYTES = 256 << 20   # calibration copy: 256 MiB read + 256 MiB written per launch
 
 
 def cpu_baseline(inp, rounds_target_s=10.0):
@@ -67,7 +74,7 @@ def cpu_baseline(inp, rounds_target_s=10.0):
     run(64)  # warm-up
     rows, elapsed, total_rows = 512, 0.0, 0
     t0 = time.perf_counter()
-    while elapsed < rounds_target_s and total_rows < 4 * inp["M"]:
+    while elapsed < rounds_target_s and total_rows < 16 * inp["M"]:
         run(rows)
         total_rows += rows
         elapsed = time.perf_counter() - t0
@@ -76,6 +83,26 @@ def cpu_baseline(inp, rounds_target_s=10.0):
             "kind": "oracle",
             "sample": f"{total_rows} tokens of the 4096-token workload in blocks of {rows} "
                       f"(rotate + quantize + fp64 product from codes), {elapsed:.1f} s"}
+
+
+def source_digest(files):
+    """sha256 over the kernel sources a traffic measurement was taken with."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(HERE, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(entry):
+    """HBM bytes per launch from the counter passes (FETCH_SIZE and WRITE_SIZE,
+    each scaled by what it reads for a copy of known size), or None when the
+    kernel sources changed since the counters were taken."""
+    if not entry or source_digest(entry["sources"]) != entry["source_digest"]:
+        return None
+    return int(round(entry["fetch_kib"] * 1024 * entry["fetch_scale"] +
+                     entry["write_kib"] * 1024 * entry["write_scale"]))
 
 
 def main():
@@ -125,6 +152,24 @@ def main():
                                M, N, K, ctypes.c_void_p(out.data_ptr()), 1, sp)
         assert st == 0, st
 
+    if args.only is not None:
+        # one kernel alone, for rocprofv3 counter passes (no timing line)
+        if args.only == "copy":
+            src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+            dst = torch.empty_like(src)
+            step = lambda i: dst.copy_(src)  # noqa: E731
+        elif args.only == "quant":
+            step = lambda i: quant(pool[i % pool_n])  # noqa: E731
+        else:
+            quant(pool[0])
+            step = lambda i: gemm()  # noqa: E731
+        for i in range(args.warmup + args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        print(json.dumps({"only": args.only, "launches": args.warmup + args.steps,
+                          "copy_bytes": COPY_BYTES if args.only == "copy" else None}), flush=True)
+        return
+
     for i in range(args.warmup):
         quant(pool[i % pool_n])
         gemm()
@@ -143,21 +188,41 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    tq = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3
-    tg = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
+    tq_step = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3
+    tg_step = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
     ms_per_step = wall / args.steps * 1e3
     flops = 2.0 * M * N * K
     quant_bytes = M * K * 2 + M * K // 2 + M * 4      # bf16 in, 4-bit codes + fp32 s out
-    gemm_tflops = flops / tg.mean() / 1e12
-    quant_gbps = quant_bytes / tq.mean() / 1e9
     value = flops / (wall / args.steps) / 1e12
 
-    traffic = None
+    # Per-kernel launch duration for the rooflines: the same kernels launched
+    # back to back on the same stream, events around the whole run, so the
+    # figure is the kernel's own duration (what a kernel trace reports)
+    # rather than the kernel plus the event gaps of the step loop.
+    def per_launch(fn, n):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(n):
+            fn(i)
+        b.record(stream)
+        b.synchronize()
+        return a.elapsed_time(b) * 1e-3 / n
+
+    n_kern = max(args.steps, 20)
+    tq = per_launch(lambda i: quant(pool[i % pool_n]), n_kern)
+    tg = per_launch(lambda i: gemm(), n_kern)
+    gemm_tflops = flops / tg / 1e12
+    quant_gbps = quant_bytes / tq / 1e9
+
+    traffic_gemm = traffic_quant = None
     if os.path.exists(args.traffic):
         try:
-            traffic = json.load(open(args.traffic)).get("qlinear_gemm_bytes")
+            tr = json.load(open(args.traffic))
+            traffic_gemm = measured_traffic(tr.get("qlinear_gemm"))
+            traffic_quant = measured_traffic(tr.get("quant_act"))
         except Exception:  # noqa: BLE001
-            traffic = None
+            traffic_gemm = traffic_quant = None
 
     line = {
         "metric": "W4A4 RPBH qlinear effective TFLOP/s + rotate/quant stage HBM GB/s",
@@ -177,13 +242,16 @@ def main():
                    "tokens": M, "d_in": K, "d_out": N, "h": h, "bits_a": 4, "bits_w": 4},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_MFMA_F16,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_MFMA_F16, 4),
-                     "traffic": traffic, "kernel": "orbit_qlinear (codebook-decode GEMM)"},
+                     "traffic": traffic_gemm, "kernel": "orbit_qlinear (codebook-decode GEMM)"},
         "roofline_quant": {"bound": "hbm", "achieved": round(quant_gbps, 1), "peak": PEAK_HBM,
                            "unit": "GB/s", "frac": round(quant_gbps / PEAK_HBM, 4),
+                           "traffic": traffic_quant,
                            "kernel": "orbit_quant_act (fused rotate + quantize)",
                            "bytes_per_launch": quant_bytes},
-        "gemm_us": round(tg.mean() * 1e6, 2),
-        "quant_us": round(tq.mean() * 1e6, 2),
+        "gemm_us": round(tg * 1e6, 2),
+        "quant_us": round(tq * 1e6, 2),
+        "step_gemm_us": round(tg_step.mean() * 1e6, 2),
+        "step_quant_us": round(tq_step.mean() * 1e6, 2),
         "quant_gbps": round(quant_gbps, 1),
         "gemm_tflops": round(gemm_tflops, 2),
     }

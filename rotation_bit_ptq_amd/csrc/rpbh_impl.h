@@ -49,6 +49,8 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+constexpr int kArgCells = 256;  // grid cells carried in the kernel arguments
+
 struct RowArgs {
   int d, h, log2h, nslots, nrounds;
   long long rows;
@@ -62,6 +64,7 @@ struct RowArgs {
   float ga, gb;  // gb already includes 2^23
   int cells, nthr;
   uint32_t grid_bias;  // 0xA8000000: turns the cell's float bits into its byte offset
+  int cells_in_args;   // 1: the grid table below was built on the host
   float thr[ORBIT_MAX_LEVELS - 1];
   uint8_t* idx_out;
   float* s_out;
@@ -74,7 +77,10 @@ struct RowArgs {
   int grid_bytes;   // LDS bytes of the grid table
   int row_bytes;    // LDS bytes of one wave's row buffer (x and -x)
   int wave_bytes;   // row buffer + transpose scratch of one wave
+  float cell_t[kArgCells];       // host-built grid (cells_in_args): thresholds
+  uint8_t cell_base[kArgCells];  // and counts of thresholds in lower cells
 };
+static_assert(sizeof(RowArgs) <= 4096, "kernel arguments must stay within 4 KB");
 
 enum Mode { kAct = 0, kWeight = 1, kRotF32 = 2, kRotF16 = 3, kInt8 = 4 };
 
@@ -82,6 +88,7 @@ struct GridCell {
   float t;   // the threshold inside the cell, +inf if none
   int base;  // thresholds in lower cells
 };
+
 
 constexpr float kMagic = 8388608.0f;  // 2^23: floats in [2^23, 2^24) are integers
 
@@ -458,10 +465,21 @@ __device__ __forceinline__ float row_alpha(const RowArgs& a, float ss, long long
 }
 
 // Grid table: cell c holds the unique threshold the float32 classification
-// puts in it (if any) and the number of thresholds in lower cells.  The
-// thresholds are read in a uniform loop (scalar loads from the kernel
-// arguments), never with per-lane indices.
+// puts in it (if any) and the number of thresholds in lower cells.  Grids of
+// up to kArgCells cells are built on the host with the same float32 cell
+// function and copied from the kernel arguments; larger ones are built here,
+// reading the thresholds in a uniform loop (scalar loads), never with
+// per-lane indices.
 __device__ __forceinline__ void build_grid(const RowArgs& a, char* smem) {
+  if (a.cells_in_args) {
+    for (int c = threadIdx.x; c < a.cells; c += blockDim.x) {
+      GridCell g;
+      g.t = a.cell_t[c];
+      g.base = a.cell_base[c];
+      ((GridCell*)smem)[c] = g;
+    }
+    return;
+  }
   const float top = kMagic + (float)(a.cells - 1);
   for (int c = threadIdx.x; c < a.cells; c += blockDim.x) {
     GridCell g;
@@ -474,6 +492,39 @@ __device__ __forceinline__ void build_grid(const RowArgs& a, char* smem) {
       if (cj == c) g.t = t;
     }
     ((GridCell*)smem)[c] = g;
+  }
+}
+
+// Byte offsets of the signed, permuted coordinates in a wave's row buffer,
+// computed once per workgroup: off[k] = (pi(k) + (D_k < 0 ? d : 0)) * size,
+// so y_k = D_k x[pi(k)] sits at wbuf + off[k].  One coalesced pass over
+// pi and the sign bits instead of per-lane scattered loads in every wave.
+template <typename InT>
+__device__ __forceinline__ void block_offsets(const RowArgs& a, uint32_t* off) {
+  for (int k = threadIdx.x; k < a.d; k += blockDim.x) {
+    const uint32_t neg = (a.sign_bits[k >> 5] >> (k & 31)) & 1u;
+    off[k] = ((uint32_t)a.perm[k] + neg * (uint32_t)a.d) * (uint32_t)sizeof(InT);
+  }
+}
+
+// The lane's gather addresses of one round from the workgroup's offsets.
+template <typename InT, int LT>
+__device__ __forceinline__ void lds_addresses(const RowArgs& a, const uint32_t* off, int slot,
+                                              uint32_t wbuf, uint32_t (&addr)[kSlot]) {
+  const int s = slot < a.nslots ? slot : 0;
+  if constexpr (LT >= 0) {
+#pragma unroll
+    for (int e = 0; e < kSlot; ++e) addr[e] = wbuf + off[tr_k<LT>(s, e)];
+  } else {
+    const u32x4* o = (const u32x4*)(off + s * kSlot);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 v = o[q];
+      addr[4 * q] = wbuf + v.x;
+      addr[4 * q + 1] = wbuf + v.y;
+      addr[4 * q + 2] = wbuf + v.z;
+      addr[4 * q + 3] = wbuf + v.w;
+    }
   }
 }
 
@@ -498,16 +549,16 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a) {
     constexpr int NCH = R * (int)sizeof(InT);  // 16-byte chunks per lane
     RowRegs<InT, NCH> pre;
     if (row < a.rows) pre.load(a, row, lane);
+    // gather offsets (overlaying the row buffers until the first row lands)
+    // and the grid table, then every lane's addresses
+    uint32_t* const off = (uint32_t*)(smem + a.grid_bytes);
+    block_offsets<InT>(a, off);
+    if constexpr (kQuant) build_grid(a, smem);
+    __syncthreads();
     uint32_t addr[R][kSlot];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      if constexpr (LT >= 0) tr_addresses<InT, LT>(a, r * kWave + lane, wbuf, addr[r]);
-      else slot_addresses<InT>(a, r * kWave + lane, wbuf, addr[r]);
-    }
-    if constexpr (kQuant) {
-      build_grid(a, smem);
-      __syncthreads();
-    }
+    for (int r = 0; r < R; ++r) lds_addresses<InT, LT>(a, off, r * kWave + lane, wbuf, addr[r]);
+    __syncthreads();
     for (; row < a.rows; row += stride) {
       pre.store(a, smem, wbuf, lane);
       if (row + stride < a.rows) pre.load(a, row + stride, lane);
@@ -596,6 +647,8 @@ hipError_t launch_typed(RowArgs a, hipStream_t stream) {
   while (waves > 1 && a.grid_bytes + waves * a.wave_bytes > di.max_lds) waves >>= 1;
   const int lds = a.grid_bytes + waves * a.wave_bytes;
   if (lds > di.max_lds) return hipErrorInvalidValue;
+  // the gather offsets (4 bytes per coordinate) overlay the row buffers
+  if (R > 0 && 4LL * a.d > (long long)waves * a.wave_bytes) return hipErrorInvalidValue;
   auto kern = rows_kernel<InT, MODE, BITS, R, LT>;
   static LaunchCache cache;
   int per_cu = 1;

@@ -1,6 +1,8 @@
 // Host entry of the row kernels (rotate, rotate + quantize, int8 pack): fills
 // the kernel arguments and dispatches on input type and mode.  The kernels
 // are in rpbh_impl.h, instantiated in the rpbh_*.hip files.
+#include <cmath>
+
 #include "rpbh_impl.h"
 
 namespace orbit {
@@ -28,6 +30,22 @@ hipError_t launch_rows(const RowJob& job, hipStream_t stream) {
   a.nthr = job.grid.nthr;
   a.grid_bias = 0xA8000000u;
   for (int i = 0; i < job.grid.nthr && job.thresholds; ++i) a.thr[i] = job.thresholds[i];
+  // small grids are built here with the kernels' float32 cell function
+  if (job.thresholds && job.grid.cells <= kArgCells) {
+    a.cells_in_args = 1;
+    for (int c = 0; c < job.grid.cells; ++c) {
+      a.cell_t[c] = INFINITY;
+      a.cell_base[c] = 0;
+    }
+    const float top = kMagic + (float)(job.grid.cells - 1);
+    for (int j = 0; j < job.grid.nthr; ++j) {
+      float f = std::fmaf(job.thresholds[j], job.grid.a, job.grid.b);
+      f = std::fmin(std::fmax(f, kMagic), top);
+      const int cj = (int)(f - kMagic);
+      a.cell_t[cj] = job.thresholds[j];
+      for (int c = cj + 1; c < job.grid.cells; ++c) a.cell_base[c] += 1;
+    }
+  }
   a.idx_out = job.idx_out;
   a.s_out = job.norm_f32_out;
   a.r_out = job.norm_bf16_out;
