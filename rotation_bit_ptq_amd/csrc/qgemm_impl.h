@@ -590,6 +590,47 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
       }
     }
   };
+  // Whole tile inside a bf16 output with 16-byte aligned rows: the tile is
+  // staged in LDS (over the decode tables, which the K loop no longer needs)
+  // and written out row by row, 16 bytes per lane, so each output row of the
+  // tile leaves as whole cache lines instead of 16-byte pieces of 32 rows.
+  // The condition is the same for every wave of the workgroup.
+  const bool staged = !f32_out && (g.N & 7) == 0 && ((uintptr_t)g.out & 15) == 0 &&
+                      (long long)(tm + 1) * TM <= g.M && (long long)(tn + 1) * TN <= g.N;
+  if (staged) {
+    constexpr int kRow = TN * 2 + 16;  // padded LDS row: 2-way bank conflicts at most
+    __syncthreads();                   // every wave is done with the tables
+    const int lm = wm * (TM / 2) + r32, ln = wn * (TN / 2) + 4 * half;
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const float4 cf = *(const float4*)(wr + 32 * j + 8 * qq);
+        const float4 cb = *(const float4*)(wb + 32 * j + 8 * qq);
+        const float cfv[4] = {cf.x, cf.y, cf.z, cf.w}, cbv[4] = {cb.x, cb.y, cb.z, cb.w};
+#pragma unroll
+        for (int i = 0; i < WM; ++i) {
+          float y[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) y[q] = __builtin_fmaf(acc[j][i][4 * qq + q], sm[i] * cfv[q], cbv[q]);
+          u32x2 w;
+          w.x = pack_bf16x2(y[0], y[1]);
+          w.y = pack_bf16x2(y[2], y[3]);
+          *(u32x2*)(smem + (lm + 32 * i) * kRow + (ln + 32 * j + 8 * qq) * 2) = w;
+        }
+      }
+    }
+    __syncthreads();
+    constexpr int kChunks = TN * 2 / 16;  // 16-byte pieces per tile row
+    char* const out0 = (char*)g.out + ((long long)tm * TM * g.N + (long long)tn * TN) * 2;
+#pragma unroll 4
+    for (int q = t; q < TM * kChunks; q += 256) {
+      const int row = q / kChunks, c = q - row * kChunks;
+      const u32x4 v = *(const u32x4*)(smem + row * kRow + c * 16);
+      *(u32x4*)(out0 + (long long)row * g.N * 2 + c * 16) = v;
+    }
+    return;
+  }
   if (fast) {
     if (f32_out) epi(std::true_type{});
     else epi(std::false_type{});
@@ -625,8 +666,11 @@ hipError_t launch_tile(GemmArgs& g, int lds, hipStream_t stream) {
   const long long tiles = (long long)g.tiles_m * g.tiles_n;
   if (tiles == 0) return hipSuccess;
   if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
-  g.factor_offset = lds;  // after the tables (a multiple of 16 KB, or 0)
-  lds += (TM + 2 * TN) * (int)sizeof(float);
+  // LDS: the decode tables (reused by the staged bf16 epilogue, which needs
+  // TM rows of TN * 2 + 16 bytes), then the tile's output factors
+  const int tile_bytes = TM * (TN * 2 + 16);
+  g.factor_offset = lds > tile_bytes ? lds : tile_bytes;  // a multiple of 16
+  lds = g.factor_offset + (TM + 2 * TN) * (int)sizeof(float);
   auto kern = gemm_kernel<KIND, OpA, OpB, WM, WN>;
   static LaunchCache cache;
   hipError_t e = prepare_launch(cache, (const void*)kern, 256, lds, nullptr);
