@@ -36,6 +36,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #include "orbit_internal.h"
 
 namespace orbit {
@@ -372,6 +374,41 @@ struct RowRegs {
     }
   }
 
+  // Sum of squares of the lane's coordinates.  Pi is orthogonal, so the
+  // row's sum over the wave is ||x'||^2 = ||x||^2 and the norm is known
+  // before the rotation.  bf16 pairs go through v_dot2c_f32_bf16 (exact
+  // products, one rounding per pair); chunks past the row end count zero.
+  __device__ __forceinline__ float sumsq(const RowArgs& a, int lane) const {
+    const int nchunk = a.d * (int)sizeof(InT) / 16;
+    float ss = 0.0f;
+    if (nchunk == NCH * kWave) {  // uniform: every chunk is part of the row
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) ss = chunk_sumsq(c[j], ss);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NCH; ++j)
+        if (lane + kWave * j < nchunk) ss = chunk_sumsq(c[j], ss);
+    }
+    return ss;
+  }
+
+  static __device__ __forceinline__ float chunk_sumsq(const u32x4& v, float ss) {
+    // the dwords go through a scalar array: a bit_cast of a subscripted
+    // vector element (v[q]) is compiled as v[0] for every q here
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if constexpr (sizeof(InT) == 2) {
+        const bf16x2 p = __builtin_bit_cast(bf16x2, w[q]);
+        ss = __builtin_amdgcn_fdot2_f32_bf16(p, p, ss, false);
+      } else {
+        const float f = __uint_as_float(w[q]);
+        ss = __builtin_fmaf(f, f, ss);
+      }
+    }
+    return ss;
+  }
+
   // writes x and -x into the wave's buffer
   __device__ __forceinline__ void store(const RowArgs& a, char* smem, uint32_t wbuf, int lane) const {
     const int nchunk = a.d * (int)sizeof(InT) / 16;
@@ -388,7 +425,10 @@ struct RowRegs {
   }
 };
 
-template <int MODE, int BITS>
+// kXrot: also write the debug copy of x' (activation mode); chosen by a
+// uniform branch around the whole row so that the plain path carries none of
+// its arithmetic.
+template <int MODE, int BITS, bool kXrot = false>
 __device__ __forceinline__ void emit_slot(const RowArgs& a, long long row, int slot, int lane,
                                           float (&v)[kSlot], float alpha, const char* smem) {
   const int d = a.d;
@@ -402,7 +442,7 @@ __device__ __forceinline__ void emit_slot(const RowArgs& a, long long row, int s
       idx[i] = g.base + (g.t < u ? 1 : 0);
     }
     store_indices<BITS>(a.idx_out + (size_t)row * ((size_t)d * BITS / 8), slot, idx);
-    if (MODE == kAct && a.xrot_f32) {
+    if constexpr (MODE == kAct && kXrot) {
       float4* o = (float4*)(a.xrot_f32 + (size_t)row * d + slot * kSlot);
 #pragma unroll
       for (int i = 0; i < kSlot; i += 4)
@@ -449,14 +489,17 @@ __device__ __forceinline__ void emit_slot(const RowArgs& a, long long row, int s
   }
 }
 
-template <int MODE>
+// ss: the sum of squares of x (kFromInput) or of the unnormalised rotated
+// values z = sqrt(h) x' (one pass per row of the long-row path).
+template <int MODE, bool kFromInput = false>
 __device__ __forceinline__ float row_alpha(const RowArgs& a, float ss, long long row, int lane) {
+  if constexpr (!kFromInput) ss *= a.inv_h;
   if constexpr (MODE == kAct) {
-    float s = sqrtf(ss * a.inv_h);
+    float s = sqrtf(ss);
     if (lane == 0) a.s_out[row] = s;
     return a.sqrt_d_over_h / (s + a.eps);
   } else if constexpr (MODE == kWeight) {
-    float r = sqrtf(ss * a.inv_h);
+    float r = sqrtf(ss);
     if (lane == 0) a.r_out[row] = f32_to_bf16_rne(r);
     return r > 0.0f ? a.sqrt_d_over_h / r : 0.0f;
   } else {
@@ -495,6 +538,11 @@ __device__ __forceinline__ void build_grid(const RowArgs& a, char* smem) {
   }
 }
 
+// Position of coordinate k in the workgroup's offset table: one pad word per
+// 128 entries, so the lane groups of a wave (whose indices differ by
+// multiples of 128) read different banks.
+__device__ __forceinline__ int off_slot(int k) { return k + (k >> 7); }
+
 // Byte offsets of the signed, permuted coordinates in a wave's row buffer,
 // computed once per workgroup: off[k] = (pi(k) + (D_k < 0 ? d : 0)) * size,
 // so y_k = D_k x[pi(k)] sits at wbuf + off[k].  One coalesced pass over
@@ -503,7 +551,7 @@ template <typename InT>
 __device__ __forceinline__ void block_offsets(const RowArgs& a, uint32_t* off) {
   for (int k = threadIdx.x; k < a.d; k += blockDim.x) {
     const uint32_t neg = (a.sign_bits[k >> 5] >> (k & 31)) & 1u;
-    off[k] = ((uint32_t)a.perm[k] + neg * (uint32_t)a.d) * (uint32_t)sizeof(InT);
+    off[off_slot(k)] = ((uint32_t)a.perm[k] + neg * (uint32_t)a.d) * (uint32_t)sizeof(InT);
   }
 }
 
@@ -514,17 +562,10 @@ __device__ __forceinline__ void lds_addresses(const RowArgs& a, const uint32_t* 
   const int s = slot < a.nslots ? slot : 0;
   if constexpr (LT >= 0) {
 #pragma unroll
-    for (int e = 0; e < kSlot; ++e) addr[e] = wbuf + off[tr_k<LT>(s, e)];
+    for (int e = 0; e < kSlot; ++e) addr[e] = wbuf + off[off_slot(tr_k<LT>(s, e))];
   } else {
-    const u32x4* o = (const u32x4*)(off + s * kSlot);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const u32x4 v = o[q];
-      addr[4 * q] = wbuf + v.x;
-      addr[4 * q + 1] = wbuf + v.y;
-      addr[4 * q + 2] = wbuf + v.z;
-      addr[4 * q + 3] = wbuf + v.w;
-    }
+    for (int e = 0; e < kSlot; ++e) addr[e] = wbuf + off[off_slot(s * kSlot + e)];
   }
 }
 
@@ -548,11 +589,41 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a) {
   if constexpr (R > 0) {
     constexpr int NCH = R * (int)sizeof(InT);  // 16-byte chunks per lane
     RowRegs<InT, NCH> pre;
+    // Gather offsets (overlaying the row buffers until the first row lands)
+    // and the grid table, then every lane's addresses.  The loads of pi and
+    // the sign bits are issued before the first row's, so waiting for them
+    // does not wait for the row.
+    // 256 threads: thread t owns coordinates 4 t + 1024 i .. + 3 (i < R), read
+    // as one 16-byte load of pi each, and the sign word of each group.
+    const bool full = blockDim.x == 256;  // uniform
+    i32x4 pv[R];
+    uint32_t sv[R];
+    if (full) {
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const int k0 = 4 * (int)threadIdx.x + 1024 * i;
+        pv[i] = k0 < a.d ? *(const i32x4*)(a.perm + k0) : i32x4{0, 0, 0, 0};
+        sv[i] = k0 < a.d ? a.sign_bits[k0 >> 5] : 0u;
+      }
+    }
     if (row < a.rows) pre.load(a, row, lane);
-    // gather offsets (overlaying the row buffers until the first row lands)
-    // and the grid table, then every lane's addresses
     uint32_t* const off = (uint32_t*)(smem + a.grid_bytes);
-    block_offsets<InT>(a, off);
+    if (full) {
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const int k0 = 4 * (int)threadIdx.x + 1024 * i;
+        if (k0 < a.d) {
+          const int pk[4] = {pv[i].x, pv[i].y, pv[i].z, pv[i].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int k = k0 + q;
+            off[off_slot(k)] = ((uint32_t)pk[q] + ((sv[i] >> (k & 31)) & 1u) * (uint32_t)a.d) * (uint32_t)sizeof(InT);
+          }
+        }
+      }
+    } else {
+      block_offsets<InT>(a, off);
+    }
     if constexpr (kQuant) build_grid(a, smem);
     __syncthreads();
     uint32_t addr[R][kSlot];
@@ -560,11 +631,15 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a) {
     for (int r = 0; r < R; ++r) lds_addresses<InT, LT>(a, off, r * kWave + lane, wbuf, addr[r]);
     __syncthreads();
     for (; row < a.rows; row += stride) {
+      float ssx = 0.0f;
+      if constexpr (kQuant) ssx = pre.sumsq(a, lane);
       pre.store(a, smem, wbuf, lane);
       if (row + stride < a.rows) pre.load(a, row + stride, lane);
+      // the norm first: its wave reduction overlaps the rotation below
+      float alpha = 0.0f;
+      if constexpr (kQuant) alpha = row_alpha<MODE, true>(a, wave_sum(ssx), row, lane);
       wave_lds_sync();
       float v[R][kSlot];
-      float ss = 0.0f;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         if constexpr (LT >= 0) {
@@ -573,19 +648,25 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a) {
           gather_h16<InT>(smem, addr[r], v[r]);
           lane_stages(v[r], lane, nstages);
         }
-        if (r * kWave + lane < a.nslots) {
-#pragma unroll
-          for (int i = 0; i < kSlot; ++i) ss = __builtin_fmaf(v[r][i], v[r][i], ss);
-        }
       }
       wave_lds_sync();  // every lane has gathered before the next row lands
-      if constexpr (kQuant) ss = wave_sum(ss);
-      const float alpha = row_alpha<MODE>(a, ss, row, lane);
+      // uniform branches: the debug copy of x', and whether every lane of
+      // every round holds a slot of the row
+      auto emit_all = [&](auto xrot) {
+        constexpr bool kX = decltype(xrot)::value;
+        if (a.nslots == R * kWave) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int slot = r * kWave + lane;
-        if (slot < a.nslots) emit_slot<MODE, BITS>(a, row, slot, lane, v[r], alpha, smem);
-      }
+          for (int r = 0; r < R; ++r) emit_slot<MODE, BITS, kX>(a, row, r * kWave + lane, lane, v[r], alpha, smem);
+        } else {
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            const int slot = r * kWave + lane;
+            if (slot < a.nslots) emit_slot<MODE, BITS, kX>(a, row, slot, lane, v[r], alpha, smem);
+          }
+        }
+      };
+      if (MODE == kAct && a.xrot_f32) emit_all(std::true_type{});
+      else emit_all(std::false_type{});
     }
   } else {
     if constexpr (kQuant) {
@@ -622,7 +703,8 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a) {
 #pragma unroll
               for (int i = 0; i < kSlot; ++i) ss = __builtin_fmaf(v[i], v[i], ss);
             } else {
-              emit_slot<MODE, BITS>(a, row, slot, lane, v, alpha, smem);
+              if (MODE == kAct && a.xrot_f32) emit_slot<MODE, BITS, true>(a, row, slot, lane, v, alpha, smem);
+              else emit_slot<MODE, BITS>(a, row, slot, lane, v, alpha, smem);
             }
           }
         }
@@ -647,8 +729,9 @@ hipError_t launch_typed(RowArgs a, hipStream_t stream) {
   while (waves > 1 && a.grid_bytes + waves * a.wave_bytes > di.max_lds) waves >>= 1;
   const int lds = a.grid_bytes + waves * a.wave_bytes;
   if (lds > di.max_lds) return hipErrorInvalidValue;
-  // the gather offsets (4 bytes per coordinate) overlay the row buffers
-  if (R > 0 && 4LL * a.d > (long long)waves * a.wave_bytes) return hipErrorInvalidValue;
+  // the gather offsets (4 bytes per coordinate plus a pad word per 128)
+  // overlay the row buffers
+  if (R > 0 && 4LL * (a.d + a.d / 128 + 1) > (long long)waves * a.wave_bytes) return hipErrorInvalidValue;
   auto kern = rows_kernel<InT, MODE, BITS, R, LT>;
   static LaunchCache cache;
   int per_cu = 1;
