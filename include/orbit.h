@@ -71,6 +71,12 @@ typedef struct {
   int32_t h;
   const int32_t *perm;
   const uint32_t *sign_bits;
+  /* Optional (NULL allowed): the rotation's gather plan, built by
+   * orbit_rpbh_build_gather for this perm, sign_bits, d and h; device,
+   * 16-byte aligned, orbit_rpbh_gather_len(d, h) entries.  With it the
+   * row kernels read each lane's gather offsets directly instead of
+   * deriving them from perm and sign_bits in every workgroup. */
+  const uint16_t *gather;
 } orbit_rpbh;
 
 #define ORBIT_MAX_D 16384
@@ -93,6 +99,25 @@ const char *orbit_status_string(orbit_status status);
 
 /* The last HIP error code seen by a failed call on this thread (0 if none). */
 int orbit_last_hip_error(void);
+
+/* Length in uint16 entries of the gather plan of a rotation of dimension d
+ * and block h: 4096 for d <= 4096 (rows kept in registers), 0 for longer
+ * rows, which take no plan.  Host only; no device use. */
+int64_t orbit_rpbh_gather_len(int32_t d, int32_t h);
+
+/* Builds the gather plan of `rot` (its `gather` field is ignored) into the
+ * device buffer `out` of orbit_rpbh_gather_len(d, h) entries, 16-byte
+ * aligned, asynchronously on `stream`.  Entry r*1024 + l*16 + e is the
+ * offset, in elements of the row buffer that holds x followed by -x, of the
+ * coordinate y_k = D_k x[perm[k]] (OrbitQuant page, Method: P_pi then the
+ * signs) that lane l gathers as element e of round r, i.e.
+ * perm[k] + (D_k = -1 ? d : 0), and 0 past the end of the row.  With
+ * s = 64 r + l: k = 16 s + e in general; for h = 64, 128 and 256 (T = h/16
+ * lanes per Hadamard block, G = 16/T, p = s mod T, e = G t + i) the order
+ * that applies H_h = H_T x H_16 as H_T first: k = 16 (s - p) + 16 t + G p + i.
+ * Errors: ORBIT_E_ARG (null or misaligned pointers), ORBIT_E_SHAPE (d, h),
+ * ORBIT_E_UNSUPPORTED (d > 4096), ORBIT_E_HIP. */
+orbit_status orbit_rpbh_build_gather(const orbit_rpbh *rot, uint16_t *out, hipStream_t stream);
 
 /* Fit the Lloyd-Max codebook for N(0,1) with 2^bits levels, in fp64, on the
  * host (OrbitQuant page, Method: Lloyd-Max run offline on the marginal).

@@ -48,7 +48,8 @@ class _Codebook(ctypes.Structure):
 
 class _RPBH(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("h", ctypes.c_int32),
-                ("perm", ctypes.c_void_p), ("sign_bits", ctypes.c_void_p)]
+                ("perm", ctypes.c_void_p), ("sign_bits", ctypes.c_void_p),
+                ("gather", ctypes.c_void_p)]
 
 
 def _load():
@@ -61,6 +62,8 @@ def _load():
         "orbit_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "orbit_last_hip_error": ([], ctypes.c_int),
         "orbit_fit_codebook": ([I32, I32, I32, D, P, P, P, P], ctypes.c_int),
+        "orbit_rpbh_gather_len": ([I32, I32], I64),
+        "orbit_rpbh_build_gather": ([P, P, P], ctypes.c_int),
         "orbit_pack_weights": ([P, P, P, ctypes.c_int, I64, I64, P, P, P], ctypes.c_int),
         "orbit_quant_act": ([P, P, P, ctypes.c_int, I64, I64, F, P, P, P, P], ctypes.c_int),
         "orbit_qlinear": ([P, P, P, P, P, P, P, ctypes.c_int, I64, I64, I64, P,
@@ -71,7 +74,11 @@ def _load():
                                P, ctypes.c_int, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
-        fn = getattr(lib, name)
+        try:
+            fn = getattr(lib, name)
+        except AttributeError as e:  # a library built from older sources
+            raise ImportError(f"{LIB_PATH} lacks {name}; rebuild it with "
+                              "__graft_entry__.build()") from e
         fn.argtypes = args
         fn.restype = res
     return lib
@@ -139,9 +146,11 @@ def fit_codebook(d: int, bits: int) -> Codebook:
 
 
 class Rotation:
-    """RPBH rotation parameters on a device: perm (gather order), sign bits, h."""
+    """RPBH rotation parameters on a device: perm (gather order), sign bits, h,
+    and (for d <= 4096, unless plan=False) the gather plan the row kernels
+    read instead of deriving their offsets from perm and the signs."""
 
-    def __init__(self, perm, signs, h: int, device="cuda"):
+    def __init__(self, perm, signs, h: int, device="cuda", plan: bool = True):
         perm = np.ascontiguousarray(perm, dtype=np.int32)
         signs = np.asarray(signs)
         d = perm.shape[0]
@@ -151,7 +160,14 @@ class Rotation:
         self.d, self.h = d, int(h)
         self.perm = torch.from_numpy(perm).to(device)
         self.sign_bits = torch.from_numpy(bits.view(np.int32)).to(device)
-        self.struct = _RPBH(d, int(h), self.perm.data_ptr(), self.sign_bits.data_ptr())
+        self.struct = _RPBH(d, int(h), self.perm.data_ptr(), self.sign_bits.data_ptr(), None)
+        self.gather = None
+        n = lib.orbit_rpbh_gather_len(d, int(h)) if plan else 0
+        if n > 0:
+            self.gather = torch.empty((n,), dtype=torch.int16, device=self.perm.device)
+            _check(lib.orbit_rpbh_build_gather(ctypes.byref(self.struct), _ptr(self.gather),
+                                               _stream(self.perm.device)), "orbit_rpbh_build_gather")
+            self.struct.gather = self.gather.data_ptr()
 
 
 def pack_weights(rot: Rotation, cw: Codebook, W: torch.Tensor):

@@ -21,6 +21,7 @@ bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
 orbit_status check_rot(const orbit_rpbh* rot, int64_t d) {
   if (!rot || !rot->perm || !rot->sign_bits || !aligned16(rot->perm)) return ORBIT_E_ARG;
+  if (rot->gather && !aligned16(rot->gather)) return ORBIT_E_ARG;
   if (rot->d != d || d < 16 || d > ORBIT_MAX_D) return ORBIT_E_SHAPE;
   if (!pow2(rot->h) || rot->h < 16 || rot->h > 1024 || d % rot->h) return ORBIT_E_SHAPE;
   return ORBIT_OK;
@@ -152,6 +153,22 @@ const char* orbit_status_string(orbit_status status) {
 
 int orbit_last_hip_error(void) { return g_last_hip_error; }
 
+int64_t orbit_rpbh_gather_len(int32_t d, int32_t h) {
+  if (d < 16 || d > 4096 || !pow2(h) || h < 16 || h > 1024 || d % h) return 0;
+  return orbit::kGatherLen;
+}
+
+orbit_status orbit_rpbh_build_gather(const orbit_rpbh* rot, uint16_t* out, hipStream_t stream) {
+  if (!rot) return ORBIT_E_ARG;
+  orbit_rpbh plain = *rot;
+  plain.gather = nullptr;
+  orbit_status st = check_rot(&plain, rot->d);
+  if (st != ORBIT_OK) return st;
+  if (rot->d > 4096) return ORBIT_E_UNSUPPORTED;
+  if (!out || !aligned16(out)) return ORBIT_E_ARG;
+  return hip_status(orbit::launch_gather_plan(rot->d, rot->h, rot->perm, rot->sign_bits, out, stream));
+}
+
 orbit_status orbit_pack_weights(const orbit_rpbh* rot, const orbit_codebook* cw, const void* W,
                                 orbit_dtype w_dtype, int64_t d_out, int64_t d_in, uint8_t* idx_out,
                                 uint16_t* r_bf16_out, hipStream_t stream) {
@@ -168,6 +185,7 @@ orbit_status orbit_pack_weights(const orbit_rpbh* rot, const orbit_codebook* cw,
   job.d = (int)d_in;
   job.h = rot->h;
   job.perm = rot->perm;
+  job.gather = rot->gather;
   job.sign_bits = rot->sign_bits;
   job.in = W;
   job.bits = cw->bits;
@@ -195,6 +213,7 @@ orbit_status orbit_quant_act(const orbit_rpbh* rot, const orbit_codebook* ca, co
   job.d = (int)d;
   job.h = rot->h;
   job.perm = rot->perm;
+  job.gather = rot->gather;
   job.sign_bits = rot->sign_bits;
   job.in = X;
   job.bits = ca->bits;
@@ -221,6 +240,7 @@ orbit_status orbit_rotate(const orbit_rpbh* rot, const void* X, orbit_dtype x_dt
   job.d = (int)d;
   job.h = rot->h;
   job.perm = rot->perm;
+  job.gather = rot->gather;
   job.sign_bits = rot->sign_bits;
   job.in = X;
   if (out_dtype == ORBIT_F32) job.xrot_f32_out = (float*)out; else job.rot_out = out;
@@ -242,6 +262,7 @@ orbit_status orbit_int8_pack_weights(const orbit_rpbh* rot, const void* W, orbit
   job.d = (int)K;
   job.h = rot->h;
   job.perm = rot->perm;
+  job.gather = rot->gather;
   job.sign_bits = rot->sign_bits;
   job.in = W;
   job.group = group;

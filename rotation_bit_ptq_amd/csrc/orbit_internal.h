@@ -51,6 +51,7 @@ struct RowJob {
   int d, h;
   const int32_t* perm;
   const uint32_t* sign_bits;
+  const uint16_t* gather;  // the rotation's gather plan, or null
   const void* in;
   // quantize outputs
   int bits;
@@ -69,6 +70,11 @@ struct RowJob {
 };
 
 hipError_t launch_rows(const RowJob& job, hipStream_t stream);
+
+// Gather plan of a rotation (rpbh_quant.hip).
+constexpr int kGatherLen = 4096;  // uint16 entries: 4 rounds x 64 lanes x 16
+hipError_t launch_gather_plan(int d, int h, const int32_t* perm, const uint32_t* sign_bits,
+                              uint16_t* out, hipStream_t stream);
 
 // ---- decode GEMMs (qgemm.hip) ----------------------------------------------
 

@@ -58,6 +58,7 @@ struct RowArgs {
   long long rows;
   const int32_t* perm;
   const uint32_t* sign_bits;
+  const uint16_t* gather;  // gather plan in this kernel's order, or null
   const void* in;
   float sqrt_d_over_h;  // sqrt(d / h): u = z * sqrt(d/h) / (s + eps), z = H y unnormalised
   float inv_sqrt_h;
@@ -589,6 +590,29 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a) {
   if constexpr (R > 0) {
     constexpr int NCH = R * (int)sizeof(InT);  // 16-byte chunks per lane
     RowRegs<InT, NCH> pre;
+    uint32_t addr[R][kSlot];
+    if (a.gather) {  // uniform: the rotation's gather plan, 32 bytes per lane and round
+      u32x4 gp[R][2];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const u32x4* src = (const u32x4*)(a.gather + r * 1024 + lane * kSlot);
+        gp[r][0] = src[0];
+        gp[r][1] = src[1];
+      }
+      if (row < a.rows) pre.load(a, row, lane);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const uint32_t w[8] = {gp[r][0].x, gp[r][0].y, gp[r][0].z, gp[r][0].w,
+                               gp[r][1].x, gp[r][1].y, gp[r][1].z, gp[r][1].w};
+#pragma unroll
+        for (int e = 0; e < kSlot; ++e)
+          addr[r][e] = wbuf + ((w[e >> 1] >> (16 * (e & 1))) & 0xffffu) * (uint32_t)sizeof(InT);
+      }
+      if constexpr (kQuant) {
+        build_grid(a, smem);
+        __syncthreads();
+      }
+    } else {
     // Gather offsets (overlaying the row buffers until the first row lands)
     // and the grid table, then every lane's addresses.  The loads of pi and
     // the sign bits are issued before the first row's, so waiting for them
@@ -626,10 +650,10 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a) {
     }
     if constexpr (kQuant) build_grid(a, smem);
     __syncthreads();
-    uint32_t addr[R][kSlot];
 #pragma unroll
     for (int r = 0; r < R; ++r) lds_addresses<InT, LT>(a, off, r * kWave + lane, wbuf, addr[r]);
     __syncthreads();
+    }
     for (; row < a.rows; row += stride) {
       float ssx = 0.0f;
       if constexpr (kQuant) ssx = pre.sumsq(a, lane);

@@ -19,6 +19,7 @@ hipError_t launch_rows(const RowJob& job, hipStream_t stream) {
   a.rows = job.rows;
   a.perm = job.perm;
   a.sign_bits = job.sign_bits;
+  a.gather = nullptr;  // set below when the plan's order is the kernel's
   a.in = job.in;
   a.sqrt_d_over_h = (float)sqrt((double)job.d / job.h);
   a.inv_sqrt_h = (float)(1.0 / sqrt((double)job.h));
@@ -62,7 +63,11 @@ hipError_t launch_rows(const RowJob& job, hipStream_t stream) {
   if (job.rows == 0) return hipSuccess;
   const bool bf16 = job.in_dtype == ORBIT_BF16;
   // bf16 rows with h = 64, 128 or 256: transposed-gather kernels
-  const bool fast = bf16 && quant && job.bits != 1 && (job.h == 64 || job.h == 128 || job.h == 256);
+  const bool tr_order = job.h == 64 || job.h == 128 || job.h == 256;
+  const bool fast = bf16 && quant && job.bits != 1 && tr_order;
+  // the gather plan serves the register-resident kernels (d <= 4096) whose
+  // gather order it was built in (transposed exactly when h allows it)
+  if (job.gather && job.d <= 4096 && fast == tr_order) a.gather = job.gather;
   if (fast) {
     const int lt = job.h == 64 ? 2 : (job.h == 128 ? 3 : 4);
     if (job.mode == RowMode::kActQuant) {
@@ -92,6 +97,35 @@ hipError_t launch_rows(const RowJob& job, hipStream_t stream) {
                   : launch_mode<float, kInt8>(a, 0, stream);
   }
   return hipErrorInvalidValue;
+}
+
+// Gather plan: entry r*1024 + l*16 + e = element offset (in the x, -x row
+// buffer) of the coordinate lane l gathers as element e of round r.
+template <int LT>
+__global__ __launch_bounds__(256) void gather_plan_kernel(int d, const int32_t* perm,
+                                                          const uint32_t* sign_bits, uint16_t* out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= kGatherLen) return;
+  const int r = i >> 10, l = (i >> 4) & 63, e = i & 15;
+  const int slot = r * rows::kWave + l;
+  uint32_t v = 0;
+  if (slot < d / rows::kSlot) {
+    int k = slot * rows::kSlot + e;
+    if constexpr (LT >= 0) k = rows::tr_k<LT>(slot, e);
+    const uint32_t neg = (sign_bits[k >> 5] >> (k & 31)) & 1u;
+    v = (uint32_t)perm[k] + neg * (uint32_t)d;
+  }
+  out[i] = (uint16_t)v;
+}
+
+hipError_t launch_gather_plan(int d, int h, const int32_t* perm, const uint32_t* sign_bits,
+                              uint16_t* out, hipStream_t stream) {
+  const dim3 grid(kGatherLen / 256), block(256);
+  if (h == 64) hipLaunchKernelGGL(gather_plan_kernel<2>, grid, block, 0, stream, d, perm, sign_bits, out);
+  else if (h == 128) hipLaunchKernelGGL(gather_plan_kernel<3>, grid, block, 0, stream, d, perm, sign_bits, out);
+  else if (h == 256) hipLaunchKernelGGL(gather_plan_kernel<4>, grid, block, 0, stream, d, perm, sign_bits, out);
+  else hipLaunchKernelGGL(gather_plan_kernel<-1>, grid, block, 0, stream, d, perm, sign_bits, out);
+  return hipGetLastError();
 }
 
 }  // namespace orbit
