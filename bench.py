@@ -85,6 +85,43 @@ def cpu_baseline(inp, rounds_target_s=10.0):
                       f"(rotate + quantize + fp64 product from codes), {elapsed:.1f} s"}
 
 
+def rotation_ablation(rbp, torch, dev, stream, M=16384, d=4096, h=128, n=20):
+    """The rotation variants of OrbitQuant's ablation (page, Experiments) on
+    the 16384 x 4096 bf16 activations of the int8 workload (d a power of two,
+    so the full RHT applies): orbit_rotate (bf16 in, fp16 out) with RPBH
+    (h = 128), Block-RHT (identity permutation) and the full RHT (h = d),
+    against a dense Haar rotation done as one bf16 GEMM by torch (timing
+    only; it is not part of the library).  Microseconds per launch."""
+    import synth
+    perm, signs = synth.rotation_params(d, 4096)
+    g = torch.Generator(device=dev).manual_seed(3)
+    X = torch.randn((M, d), generator=g, device=dev).to(torch.bfloat16)
+    out = torch.empty((M, d), dtype=torch.float16, device=dev)
+    Q = torch.linalg.qr(torch.randn((d, d), generator=g, device=dev))[0].to(torch.bfloat16)
+    rots = {"rpbh_h128": rbp.Rotation(perm, signs, h),
+            "block_rht_h128": rbp.Rotation(np.arange(d, dtype=np.int32), signs, h),
+            "full_rht_h4096": rbp.Rotation(perm, signs, d)}
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        b.synchronize()
+        return a.elapsed_time(b) * 1e3 / n
+
+    res = {k: round(timed(lambda r=r: rbp.rotate(r, X, out_dtype=torch.float16, out=out)), 2)
+           for k, r in rots.items()}
+    res["haar_dense_bf16_gemm"] = round(timed(lambda: torch.matmul(X, Q)), 2)
+    res["bytes_per_launch"] = M * d * 4
+    res["unit"] = "us"
+    return res
+
+
 def source_digest(files):
     """sha256 over the kernel sources a traffic measurement was taken with."""
     import hashlib
@@ -255,6 +292,7 @@ def main():
         "quant_gbps": round(quant_gbps, 1),
         "gemm_tflops": round(gemm_tflops, 2),
     }
+    line["rotation_ablation"] = rotation_ablation(rbp, torch, dev, stream)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(line), flush=True)

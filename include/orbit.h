@@ -59,13 +59,14 @@ typedef enum { ORBIT_F32 = 0, ORBIT_BF16 = 1, ORBIT_F16 = 2 } orbit_dtype;
 
 /* RPBH rotation parameters (the int8 article's "rotation metadata").
  * d: dimension, a multiple of h, 16 <= d <= ORBIT_MAX_D.
- * h: Hadamard block size, a power of two, 16 <= h <= 1024.
+ * h: Hadamard block size, a power of two, 16 <= h <= 1024, or 2048 / 4096
+ *    when d <= 4096.
  * perm: device int32[d], a permutation of 0..d-1 (gather order).
  * sign_bits: device uint32[(d + 31) / 32]; bit k%32 of word k/32 set means
  *            D_k = -1 for permuted coordinate k.
  * Variants of the rotation ablation (OrbitQuant page, Experiments): an
  * identity perm gives Block-RHT, h = d gives the full RHT (d a power of two
- * up to 1024). */
+ * up to 4096). */
 typedef struct {
   int32_t d;
   int32_t h;

@@ -23,7 +23,8 @@ orbit_status check_rot(const orbit_rpbh* rot, int64_t d) {
   if (!rot || !rot->perm || !rot->sign_bits || !aligned16(rot->perm)) return ORBIT_E_ARG;
   if (rot->gather && !aligned16(rot->gather)) return ORBIT_E_ARG;
   if (rot->d != d || d < 16 || d > ORBIT_MAX_D) return ORBIT_E_SHAPE;
-  if (!pow2(rot->h) || rot->h < 16 || rot->h > 1024 || d % rot->h) return ORBIT_E_SHAPE;
+  if (!pow2(rot->h) || rot->h < 16 || rot->h > 4096 || d % rot->h) return ORBIT_E_SHAPE;
+  if (rot->h > 1024 && d > 4096) return ORBIT_E_SHAPE;  // long blocks: rows kept in registers
   return ORBIT_OK;
 }
 
@@ -154,7 +155,7 @@ const char* orbit_status_string(orbit_status status) {
 int orbit_last_hip_error(void) { return g_last_hip_error; }
 
 int64_t orbit_rpbh_gather_len(int32_t d, int32_t h) {
-  if (d < 16 || d > 4096 || !pow2(h) || h < 16 || h > 1024 || d % h) return 0;
+  if (d < 16 || d > 4096 || !pow2(h) || h < 16 || h > 4096 || d % h) return 0;
   return orbit::kGatherLen;
 }
 

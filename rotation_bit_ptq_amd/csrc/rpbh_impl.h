@@ -187,6 +187,28 @@ __device__ __forceinline__ void lane_stages(float (&v)[kSlot], int lane, int nst
   if (nstages > 5) lane_stage<32>(v, lane);
 }
 
+// Blocks longer than one round (h = 1024 n, n = 2 or 4): in Sylvester order
+// H_h = H_n (x) H_1024 and round r holds positions 1024 r .. 1024 r + 1023,
+// so after H_1024 inside every round the remaining stages pair rounds
+// r and r + span, element by element, in registers.
+template <int R>
+__device__ __forceinline__ void round_stages(float (&v)[R][kSlot], int n) {
+#pragma unroll
+  for (int span = 1; span < R; span <<= 1) {
+    if (span >= n) break;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (r & span) continue;
+#pragma unroll
+      for (int i = 0; i < kSlot; ++i) {
+        const float x = v[r][i], y = v[r + span][i];
+        v[r][i] = x + y;
+        v[r + span][i] = x - y;
+      }
+    }
+  }
+}
+
 // Butterfly stages of span `from` .. 8 inside the lane's 16 values.
 __device__ __forceinline__ void slot_stages(float (&v)[kSlot], int from) {
 #pragma unroll
@@ -673,6 +695,9 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a) {
           lane_stages(v[r], lane, nstages);
         }
       }
+      if constexpr (LT < 0 && R > 1) {
+        if (a.h > 1024) round_stages<R>(v, a.h >> 10);  // uniform: h = 2048, 4096
+      }
       wave_lds_sync();  // every lane has gathered before the next row lands
       // uniform branches: the debug copy of x', and whether every lane of
       // every round holds a slot of the row
@@ -810,6 +835,14 @@ hipError_t launch_fast(const RowArgs& a, int bits, hipStream_t stream);
       case 8: return launch_fast_rounds<MODE, 8, LT>(a, s);                 \
     }                                                                       \
     return hipErrorInvalidValue;                                            \
+  }
+
+// Rotation-only and int8-pack modes of the transposed-gather kernels (no
+// code width: BITS is unused by these modes).
+#define ORBIT_ROWS_FAST_PLAIN(MODE, LT)                                       \
+  template <>                                                               \
+  hipError_t launch_fast<MODE, LT>(const RowArgs& a, int, hipStream_t s) {  \
+    return launch_fast_rounds<MODE, 4, LT>(a, s);                           \
   }
 
 // Instantiated per (input type, mode) in the rpbh_*.hip files.

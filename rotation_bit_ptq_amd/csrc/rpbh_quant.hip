@@ -64,7 +64,7 @@ hipError_t launch_rows(const RowJob& job, hipStream_t stream) {
   const bool bf16 = job.in_dtype == ORBIT_BF16;
   // bf16 rows with h = 64, 128 or 256: transposed-gather kernels
   const bool tr_order = job.h == 64 || job.h == 128 || job.h == 256;
-  const bool fast = bf16 && quant && job.bits != 1 && tr_order;
+  const bool fast = bf16 && tr_order && (!quant || job.bits != 1);
   // the gather plan serves the register-resident kernels (d <= 4096) whose
   // gather order it was built in (transposed exactly when h allows it)
   if (job.gather && job.d <= 4096 && fast == tr_order) a.gather = job.gather;
@@ -75,9 +75,24 @@ hipError_t launch_rows(const RowJob& job, hipStream_t stream) {
       if (lt == 3) return launch_fast<kAct, 3>(a, job.bits, stream);
       return launch_fast<kAct, 4>(a, job.bits, stream);
     }
-    if (lt == 2) return launch_fast<kWeight, 2>(a, job.bits, stream);
-    if (lt == 3) return launch_fast<kWeight, 3>(a, job.bits, stream);
-    return launch_fast<kWeight, 4>(a, job.bits, stream);
+    if (job.mode == RowMode::kWeightQuant) {
+      if (lt == 2) return launch_fast<kWeight, 2>(a, job.bits, stream);
+      if (lt == 3) return launch_fast<kWeight, 3>(a, job.bits, stream);
+      return launch_fast<kWeight, 4>(a, job.bits, stream);
+    }
+    if (job.mode == RowMode::kInt8Pack) {
+      if (lt == 2) return launch_fast<kInt8, 2>(a, 0, stream);
+      if (lt == 3) return launch_fast<kInt8, 3>(a, 0, stream);
+      return launch_fast<kInt8, 4>(a, 0, stream);
+    }
+    if (job.out_dtype == ORBIT_F16) {
+      if (lt == 2) return launch_fast<kRotF16, 2>(a, 0, stream);
+      if (lt == 3) return launch_fast<kRotF16, 3>(a, 0, stream);
+      return launch_fast<kRotF16, 4>(a, 0, stream);
+    }
+    if (lt == 2) return launch_fast<kRotF32, 2>(a, 0, stream);
+    if (lt == 3) return launch_fast<kRotF32, 3>(a, 0, stream);
+    return launch_fast<kRotF32, 4>(a, 0, stream);
   }
   switch (job.mode) {
     case RowMode::kActQuant:

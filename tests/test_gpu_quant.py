@@ -65,12 +65,34 @@ def test_quant_act_long_rows_two_pass(gpu_lib):
     _run_act(gpu_lib, X, inp["perm2"], inp["signs2"], 256, 4, "down-d12288")
 
 
-@pytest.mark.parametrize("d,h", [(1040, 16), (48, 16), (3072, 32), (3072, 1024), (1024, 1024)])
+@pytest.mark.parametrize("d,h", [(1040, 16), (48, 16), (3072, 32), (3072, 1024), (1024, 1024),
+                                 (2048, 2048), (4096, 4096), (4096, 2048)])
 def test_quant_act_shapes(gpu_lib, d, h):
     perm, signs = synth.rotation_params(d, 100 + d + h)
     g = np.random.default_rng(d + h)
     X = synth.f32_to_bf16_bits(g.standard_normal((70, d)).astype(np.float32))
     _run_act(gpu_lib, X, perm, signs, h, 4, f"d{d}-h{h}")
+
+
+@pytest.mark.parametrize("d", [2048, 4096])
+def test_full_rht_rotate_and_weights(gpu_lib, d):
+    """Full RHT (OrbitQuant page, Experiments: the rotation ablation), h = d:
+    rotations and weight codes against the oracle's full_rht_rotate."""
+    rbp = gpu_lib
+    perm, signs = synth.rotation_params(d, 40 + d)
+    g = np.random.default_rng(d)
+    X = synth.f32_to_bf16_bits(g.standard_normal((48, d)).astype(np.float32))
+    rot = rbp.Rotation(perm, signs, d)
+    ref = oracle.full_rht_rotate(as_f64(X), perm, signs)
+    for dt, tol in ((torch.float32, 1e-5), (torch.float16, 2e-3)):
+        y = rbp.rotate(rot, to_dev(X), out_dtype=dt).cpu().numpy().astype(np.float64)
+        err = np.linalg.norm(y - ref, axis=1) / np.linalg.norm(ref, axis=1)
+        assert np.all(err <= tol), f"full RHT d={d} {dt}: {err.max()}"
+    cb = rbp.Codebook(d, 4)
+    ref_cb = oracle.codebook(4)
+    idx, r = rbp.pack_weights(rot, cb, to_dev(X))
+    wref = oracle.pack_weights(as_f64(X), perm, signs, d, ref_cb, 4)
+    check_indices(idx, 4, d, wref["u"], ref_cb["thresholds"], f"full-rht-w{d}")
 
 
 def test_block_rht_identity_permutation(gpu_lib):
