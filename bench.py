@@ -122,6 +122,63 @@ def rotation_ablation(rbp, torch, dev, stream, M=16384, d=4096, h=128, n=20):
     return res
 
 
+def mlp_pair(rbp, torch, dev, stream, n=3):
+    """The DiT MLP pair at its real shape: 16384 tokens, up 3072 -> 12288
+    (W2A4, h = 256), GELU, down 12288 -> 3072 (W2A4, h = 256, 48 blocks).
+    Fused: GELU in the up GEMM's epilogue and the down layer's permutation
+    folded into the up layer's weight rows, so the down quantizer runs with
+    the identity permutation on the up output as written.  Unfused: the up
+    GEMM, a separate GELU pass (torch, bf16 in and out), the down quantizer
+    with its permutation.  Microseconds per pair and effective TFLOP/s."""
+    import synth
+    inp = synth.make(4)
+    M, K, N = inp["M"], inp["K"], inp["N"]
+    to = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    X, W_up, W_dn = to(inp["X"]), to(inp["W"]), to(inp["W2"])
+    perm2 = inp["perm2"]
+    rot_up = rbp.Rotation(inp["perm"], inp["signs"], 256)
+    rot_dn = rbp.Rotation(perm2, inp["signs2"], 256)
+    rot_dn_f = rbp.Rotation(np.arange(N, dtype=np.int32), inp["signs2"], 256)
+    ca_up, cw_up = rbp.Codebook(K, 4), rbp.Codebook(K, 2)
+    ca_dn, cw_dn = rbp.Codebook(N, 4), rbp.Codebook(N, 2)
+    iw_up, r_up = rbp.pack_weights(rot_up, cw_up, W_up)
+    iw_upf, r_upf = rbp.pack_weights(rot_up, cw_up,
+                                     W_up[torch.from_numpy(perm2).long().to(dev)].contiguous())
+    iw_dn, r_dn = rbp.pack_weights(rot_dn, cw_dn, W_dn)
+    H = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+
+    def fused():
+        ia, s = rbp.quant_act(rot_up, ca_up, X)
+        rbp.qlinear(ia, s, ca_up, iw_upf, r_upf, cw_up, K, out=H, act="gelu")
+        ib, s2 = rbp.quant_act(rot_dn_f, ca_dn, H)
+        rbp.qlinear(ib, s2, ca_dn, iw_dn, r_dn, cw_dn, N, out=out)
+
+    def unfused():
+        ia, s = rbp.quant_act(rot_up, ca_up, X)
+        rbp.qlinear(ia, s, ca_up, iw_up, r_up, cw_up, K, out=H)
+        G = torch.nn.functional.gelu(H)
+        ib, s2 = rbp.quant_act(rot_dn, ca_dn, G)
+        rbp.qlinear(ib, s2, ca_dn, iw_dn, r_dn, cw_dn, N, out=out)
+
+    def timed(fn):
+        fn()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        b.synchronize()
+        return a.elapsed_time(b) * 1e3 / n
+
+    tf, tu = timed(fused), timed(unfused)
+    flops = 2.0 * 2 * M * K * N
+    return {"workload": "MLP pair W2A4: 16384 tokens, 3072 -> 12288 -> 3072, h = 256, GELU",
+            "fused_us": round(tf, 1), "unfused_us": round(tu, 1),
+            "fused_tflops": round(flops / tf / 1e6, 1), "unfused_tflops": round(flops / tu / 1e6, 1)}
+
+
 def source_digest(files):
     """sha256 over the kernel sources a traffic measurement was taken with."""
     import hashlib
@@ -293,6 +350,7 @@ def main():
         "gemm_tflops": round(gemm_tflops, 2),
     }
     line["rotation_ablation"] = rotation_ablation(rbp, torch, dev, stream)
+    line["mlp_pair"] = mlp_pair(rbp, torch, dev, stream)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(line), flush=True)

@@ -102,8 +102,8 @@ const char *orbit_status_string(orbit_status status);
 int orbit_last_hip_error(void);
 
 /* Length in uint16 entries of the gather plan of a rotation of dimension d
- * and block h: 4096 for d <= 4096 (rows kept in registers), 0 for longer
- * rows, which take no plan.  Host only; no device use. */
+ * and block h: 1024 per round of 1024 coordinates, at least 4096
+ * (1024 * max(4, ceil(d / 1024))); 0 for invalid d, h.  Host only. */
 int64_t orbit_rpbh_gather_len(int32_t d, int32_t h);
 
 /* Builds the gather plan of `rot` (its `gather` field is ignored) into the
@@ -117,7 +117,7 @@ int64_t orbit_rpbh_gather_len(int32_t d, int32_t h);
  * lanes per Hadamard block, G = 16/T, p = s mod T, e = G t + i) the order
  * that applies H_h = H_T x H_16 as H_T first: k = 16 (s - p) + 16 t + G p + i.
  * Errors: ORBIT_E_ARG (null or misaligned pointers), ORBIT_E_SHAPE (d, h),
- * ORBIT_E_UNSUPPORTED (d > 4096), ORBIT_E_HIP. */
+ * ORBIT_E_HIP. */
 orbit_status orbit_rpbh_build_gather(const orbit_rpbh *rot, uint16_t *out, hipStream_t stream);
 
 /* Fit the Lloyd-Max codebook for N(0,1) with 2^bits levels, in fp64, on the
@@ -169,6 +169,21 @@ orbit_status orbit_qlinear(const uint8_t *idx_a, const float *s, const orbit_cod
                            const orbit_codebook *cw, const void *bias, orbit_dtype bias_dtype,
                            int64_t M, int64_t N, int64_t K, void *out, orbit_dtype out_dtype,
                            hipStream_t stream);
+
+/* Output activation of orbit_qlinear_act. */
+typedef enum { ORBIT_ACT_NONE = 0, ORBIT_ACT_GELU = 1 } orbit_act;
+
+/* orbit_qlinear with an elementwise activation applied in fp32 to
+ * s_m r_n / K * acc (+ bias) before the single rounding of the output:
+ * ORBIT_ACT_GELU is the erf GELU, x/2 (1 + erf(x / sqrt 2)), the activation
+ * between the two layers of a DiT MLP.  Fusing it here removes the separate
+ * activation pass over the hidden activations.  Same arguments, layouts and
+ * errors as orbit_qlinear, plus ORBIT_E_ARG for an unknown act. */
+orbit_status orbit_qlinear_act(const uint8_t *idx_a, const float *s, const orbit_codebook *ca,
+                               const uint8_t *idx_w, const uint16_t *r_bf16,
+                               const orbit_codebook *cw, const void *bias, orbit_dtype bias_dtype,
+                               int64_t M, int64_t N, int64_t K, void *out, orbit_dtype out_dtype,
+                               orbit_act act, hipStream_t stream);
 
 /* Rotation alone: out = Pi x per row (the int8 path's run-time step, and a
  * debugging aid).  X: device [M, d] F32 or BF16; out: device [M, d],

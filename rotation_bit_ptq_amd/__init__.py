@@ -68,6 +68,8 @@ def _load():
         "orbit_quant_act": ([P, P, P, ctypes.c_int, I64, I64, F, P, P, P, P], ctypes.c_int),
         "orbit_qlinear": ([P, P, P, P, P, P, P, ctypes.c_int, I64, I64, I64, P,
                            ctypes.c_int, P], ctypes.c_int),
+        "orbit_qlinear_act": ([P, P, P, P, P, P, P, ctypes.c_int, I64, I64, I64, P,
+                               ctypes.c_int, ctypes.c_int, P], ctypes.c_int),
         "orbit_rotate": ([P, P, ctypes.c_int, I64, I64, P, ctypes.c_int, P], ctypes.c_int),
         "orbit_int8_pack_weights": ([P, P, ctypes.c_int, I64, I64, I32, P, P, P], ctypes.c_int),
         "orbit_int8_linear": ([P, ctypes.c_int, I64, I64, P, P, I32, I64, P, ctypes.c_int,
@@ -196,18 +198,24 @@ def quant_act(rot: Rotation, ca: Codebook, X: torch.Tensor, eps: float = 1e-8,
     return (idx, s, xr) if debug_xrot else (idx, s)
 
 
+ACTS = {None: 0, "gelu": 1}
+
+
 def qlinear(idx_a, s, ca: Codebook, idx_w, r, cw: Codebook, K: int, bias=None,
-            out_dtype=torch.bfloat16, out=None):
-    """out[m, n] = s_m r_n / K * sum_k ca[ia] cw[iw] (+ bias)."""
+            out_dtype=torch.bfloat16, out=None, act=None):
+    """out[m, n] = act(s_m r_n / K * sum_k ca[ia] cw[iw] (+ bias)); act None or "gelu"."""
     for t, n in ((idx_a, "idx_a"), (s, "s"), (idx_w, "idx_w"), (r, "r")):
         _dev(t, n)
+    if act not in ACTS:
+        raise OrbitError(f"unknown activation {act!r}")
     M, N = idx_a.shape[0], idx_w.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=idx_a.device)
     bias_dt = _DT[bias.dtype] if bias is not None else F32
-    _check(lib.orbit_qlinear(_ptr(idx_a), _ptr(s), ctypes.byref(ca.struct), _ptr(idx_w), _ptr(r),
-                             ctypes.byref(cw.struct), _ptr(bias), bias_dt, M, N, K, _ptr(out),
-                             _DT[out.dtype], _stream(idx_a.device)), "orbit_qlinear")
+    _check(lib.orbit_qlinear_act(_ptr(idx_a), _ptr(s), ctypes.byref(ca.struct), _ptr(idx_w),
+                                 _ptr(r), ctypes.byref(cw.struct), _ptr(bias), bias_dt, M, N, K,
+                                 _ptr(out), _DT[out.dtype], ACTS[act], _stream(idx_a.device)),
+           "orbit_qlinear_act")
     return out
 
 

@@ -155,8 +155,9 @@ const char* orbit_status_string(orbit_status status) {
 int orbit_last_hip_error(void) { return g_last_hip_error; }
 
 int64_t orbit_rpbh_gather_len(int32_t d, int32_t h) {
-  if (d < 16 || d > 4096 || !pow2(h) || h < 16 || h > 4096 || d % h) return 0;
-  return orbit::kGatherLen;
+  if (d < 16 || d > ORBIT_MAX_D || !pow2(h) || h < 16 || h > 4096 || d % h) return 0;
+  if (h > 1024 && d > 4096) return 0;
+  return orbit::gather_len(d);
 }
 
 orbit_status orbit_rpbh_build_gather(const orbit_rpbh* rot, uint16_t* out, hipStream_t stream) {
@@ -165,7 +166,6 @@ orbit_status orbit_rpbh_build_gather(const orbit_rpbh* rot, uint16_t* out, hipSt
   plain.gather = nullptr;
   orbit_status st = check_rot(&plain, rot->d);
   if (st != ORBIT_OK) return st;
-  if (rot->d > 4096) return ORBIT_E_UNSUPPORTED;
   if (!out || !aligned16(out)) return ORBIT_E_ARG;
   return hip_status(orbit::launch_gather_plan(rot->d, rot->h, rot->perm, rot->sign_bits, out, stream));
 }
@@ -272,11 +272,13 @@ orbit_status orbit_int8_pack_weights(const orbit_rpbh* rot, const void* W, orbit
   return hip_status(orbit::launch_rows(job, stream));
 }
 
-orbit_status orbit_qlinear(const uint8_t* idx_a, const float* s, const orbit_codebook* ca,
-                           const uint8_t* idx_w, const uint16_t* r_bf16, const orbit_codebook* cw,
-                           const void* bias, orbit_dtype bias_dtype, int64_t M, int64_t N, int64_t K,
-                           void* out, orbit_dtype out_dtype, hipStream_t stream) {
+orbit_status orbit_qlinear_act(const uint8_t* idx_a, const float* s, const orbit_codebook* ca,
+                               const uint8_t* idx_w, const uint16_t* r_bf16,
+                               const orbit_codebook* cw, const void* bias, orbit_dtype bias_dtype,
+                               int64_t M, int64_t N, int64_t K, void* out, orbit_dtype out_dtype,
+                               orbit_act act, hipStream_t stream) {
   orbit_status st;
+  if (act != ORBIT_ACT_NONE && act != ORBIT_ACT_GELU) return ORBIT_E_ARG;
   if ((st = check_codebook(ca)) != ORBIT_OK) return st;
   if ((st = check_codebook(cw)) != ORBIT_OK) return st;
   if (ca->bits == 1 || cw->bits == 1) return ORBIT_E_UNSUPPORTED;
@@ -307,7 +309,16 @@ orbit_status orbit_qlinear(const uint8_t* idx_a, const float* s, const orbit_cod
   job.bias_dtype = bias_dtype;
   job.out = out;
   job.out_dtype = out_dtype;
+  job.act = act;
   return hip_status(orbit::launch_gemm(job, stream));
+}
+
+orbit_status orbit_qlinear(const uint8_t* idx_a, const float* s, const orbit_codebook* ca,
+                           const uint8_t* idx_w, const uint16_t* r_bf16, const orbit_codebook* cw,
+                           const void* bias, orbit_dtype bias_dtype, int64_t M, int64_t N, int64_t K,
+                           void* out, orbit_dtype out_dtype, hipStream_t stream) {
+  return orbit_qlinear_act(idx_a, s, ca, idx_w, r_bf16, cw, bias, bias_dtype, M, N, K, out,
+                           out_dtype, ORBIT_ACT_NONE, stream);
 }
 
 orbit_status orbit_int8_linear(const void* Xrot, orbit_dtype xrot_dtype, int64_t M, int64_t K,

@@ -71,8 +71,12 @@ struct RowJob {
 
 hipError_t launch_rows(const RowJob& job, hipStream_t stream);
 
-// Gather plan of a rotation (rpbh_quant.hip).
-constexpr int kGatherLen = 4096;  // uint16 entries: 4 rounds x 64 lanes x 16
+// Gather plan of a rotation (rpbh_quant.hip): 1024 uint16 entries (64 lanes
+// x 16) per round of the row, at least 4 rounds.
+__host__ __device__ inline int gather_len(int d) {
+  const int rounds = (d + 1023) / 1024;
+  return 1024 * (rounds < 4 ? 4 : rounds);
+}
 hipError_t launch_gather_plan(int d, int h, const int32_t* perm, const uint32_t* sign_bits,
                               uint16_t* out, hipStream_t stream);
 
@@ -94,6 +98,7 @@ struct GemmJob {
   int bias_dtype;
   void* out;
   int out_dtype;
+  int act;  // orbit_act, applied in the epilogue
 };
 
 hipError_t launch_gemm(const GemmJob& job, hipStream_t stream);

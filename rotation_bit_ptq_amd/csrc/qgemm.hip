@@ -28,6 +28,7 @@ hipError_t launch_gemm(const GemmJob& job, hipStream_t stream) {
   g.bias_dtype = job.bias_dtype;
   g.out = job.out;
   g.out_dtype = job.out_dtype;
+  g.act = job.act;
   if (job.M == 0 || job.N == 0) return hipSuccess;
   if (job.kind == 0) {
     g.lda = job.K * job.bits_a / 8;

@@ -59,6 +59,7 @@ struct GemmArgs {
   int bias_dtype;
   void* out;
   int out_dtype;
+  int act;  // orbit_act
   int tiles_m, tiles_n;
   int table_a_offset;  // LDS byte offset of the activation codebook table
   int table_b_offset;  // LDS byte offset of the weight codebook table
@@ -262,6 +263,34 @@ __device__ __forceinline__ float load_bias(const GemmArgs& g, long long n) {
   if (!g.bias) return 0.0f;
   if (g.bias_dtype == ORBIT_BF16) return __uint_as_float((uint32_t)((const uint16_t*)g.bias)[n] << 16);
   return ((const float*)g.bias)[n];
+}
+
+// erf by Abramowitz & Stegun, Handbook of Mathematical Functions, 7.1.26:
+// erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),
+// t = 1 / (1 + p x) for x >= 0, odd extension; |error| <= 1.5e-7.  Branch
+// free: one reciprocal, one exp2 and a Horner polynomial, far below the bf16
+// rounding of the output it feeds.
+__device__ __forceinline__ float erf_as7126(float x) {
+  const float ax = __builtin_fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f, ax, 1.0f));
+  float p = __builtin_fmaf(1.061405429f, t, -1.453152027f);
+  p = __builtin_fmaf(p, t, 1.421413741f);
+  p = __builtin_fmaf(p, t, -0.284496736f);
+  p = __builtin_fmaf(p, t, 0.254829592f);
+  p *= t;
+  const float e = __builtin_amdgcn_exp2f(-(ax * ax) * 1.4426950408889634f);  // exp(-x^2)
+  return __builtin_copysignf(__builtin_fmaf(-p, e, 1.0f), x);
+}
+
+// Output activation applied in fp32 before the output is rounded.
+template <int ACT>
+__device__ __forceinline__ float act_fn(float y) {
+  if constexpr (ACT == ORBIT_ACT_GELU) {
+    const float h = 0.5f * y;
+    return __builtin_fmaf(h, erf_as7126(y * 0.70710678118654752f), h);  // y/2 (1 + erf(y/sqrt 2))
+  } else {
+    return y;
+  }
 }
 
 // Tile order: consecutive workgroups land on different XCDs (round robin), so
@@ -559,103 +588,109 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
   float sm[WM];
 #pragma unroll
   for (int i = 0; i < WM; ++i) sm[i] = ws[32 * i];
-  const bool f32_out = g.out_dtype != ORBIT_BF16;
-  const bool fast = (g.N & 3) == 0 && ((uintptr_t)g.out & 15) == 0 && m_base + TM / 2 <= g.M &&
-                    n_base + TN / 2 <= g.N;
-  auto epi = [&](auto f32c) {
-    constexpr bool F32 = decltype(f32c)::value;
+  // the whole output path, for one activation (uniform choice below)
+  auto finish = [&](auto actc) {
+    constexpr int ACT = decltype(actc)::value;
+    const bool f32_out = g.out_dtype != ORBIT_BF16;
+    const bool fast = (g.N & 3) == 0 && ((uintptr_t)g.out & 15) == 0 && m_base + TM / 2 <= g.M &&
+                      n_base + TN / 2 <= g.N;
+    auto epi = [&](auto f32c) {
+      constexpr bool F32 = decltype(f32c)::value;
+#pragma unroll
+      for (int j = 0; j < WN; ++j) {
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const long long n0 = n_base + 32 * j + 8 * qq + 4 * half;
+          const float4 cf = *(const float4*)(wr + 32 * j + 8 * qq);
+          const float4 cb = *(const float4*)(wb + 32 * j + 8 * qq);
+          const float cfv[4] = {cf.x, cf.y, cf.z, cf.w}, cbv[4] = {cb.x, cb.y, cb.z, cb.w};
+#pragma unroll
+          for (int i = 0; i < WM; ++i) {
+            const long long m = m_base + 32 * i + r32;
+            float y[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) y[q] = act_fn<ACT>(__builtin_fmaf(acc[j][i][4 * qq + q], sm[i] * cfv[q], cbv[q]));
+            if constexpr (F32) {
+              *(float4*)((float*)g.out + m * g.N + n0) = make_float4(y[0], y[1], y[2], y[3]);
+            } else {
+              u32x2 w;
+              w.x = pack_bf16x2(y[0], y[1]);
+              w.y = pack_bf16x2(y[2], y[3]);
+              *(u32x2*)((uint16_t*)g.out + m * g.N + n0) = w;
+            }
+          }
+        }
+      }
+    };
+    // Whole tile inside a bf16 output with 16-byte aligned rows: the tile is
+    // staged in LDS (over the decode tables, which the K loop no longer needs)
+    // and written out row by row, 16 bytes per lane, so each output row of the
+    // tile leaves as whole cache lines instead of 16-byte pieces of 32 rows.
+    // The condition is the same for every wave of the workgroup.
+    const bool staged = !f32_out && (g.N & 7) == 0 && ((uintptr_t)g.out & 15) == 0 &&
+                        (long long)(tm + 1) * TM <= g.M && (long long)(tn + 1) * TN <= g.N;
+    if (staged) {
+      constexpr int kRow = TN * 2 + 16;  // padded LDS row: 2-way bank conflicts at most
+      __syncthreads();                   // every wave is done with the tables
+      const int lm = wm * (TM / 2) + r32, ln = wn * (TN / 2) + 4 * half;
+#pragma unroll
+      for (int j = 0; j < WN; ++j) {
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const float4 cf = *(const float4*)(wr + 32 * j + 8 * qq);
+          const float4 cb = *(const float4*)(wb + 32 * j + 8 * qq);
+          const float cfv[4] = {cf.x, cf.y, cf.z, cf.w}, cbv[4] = {cb.x, cb.y, cb.z, cb.w};
+#pragma unroll
+          for (int i = 0; i < WM; ++i) {
+            float y[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) y[q] = act_fn<ACT>(__builtin_fmaf(acc[j][i][4 * qq + q], sm[i] * cfv[q], cbv[q]));
+            u32x2 w;
+            w.x = pack_bf16x2(y[0], y[1]);
+            w.y = pack_bf16x2(y[2], y[3]);
+            *(u32x2*)(smem + (lm + 32 * i) * kRow + (ln + 32 * j + 8 * qq) * 2) = w;
+          }
+        }
+      }
+      __syncthreads();
+      constexpr int kChunks = TN * 2 / 16;  // 16-byte pieces per tile row
+      char* const out0 = (char*)g.out + ((long long)tm * TM * g.N + (long long)tn * TN) * 2;
+#pragma unroll 4
+      for (int q = t; q < TM * kChunks; q += 256) {
+        const int row = q / kChunks, c = q - row * kChunks;
+        const u32x4 v = *(const u32x4*)(smem + row * kRow + c * 16);
+        *(u32x4*)(out0 + (long long)row * g.N * 2 + c * 16) = v;
+      }
+      return;
+    }
+    if (fast) {
+      if (f32_out) epi(std::true_type{});
+      else epi(std::false_type{});
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
-        const long long n0 = n_base + 32 * j + 8 * qq + 4 * half;
-        const float4 cf = *(const float4*)(wr + 32 * j + 8 * qq);
-        const float4 cb = *(const float4*)(wb + 32 * j + 8 * qq);
-        const float cfv[4] = {cf.x, cf.y, cf.z, cf.w}, cbv[4] = {cb.x, cb.y, cb.z, cb.w};
 #pragma unroll
-        for (int i = 0; i < WM; ++i) {
-          const long long m = m_base + 32 * i + r32;
-          float y[4];
+        for (int q = 0; q < 4; ++q) {
+          const long long n = n_base + 32 * j + 8 * qq + 4 * half + q;
+          if (n >= g.N) continue;
+          const float cf = wr[32 * j + 8 * qq + q], cb = wb[32 * j + 8 * qq + q];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) y[q] = __builtin_fmaf(acc[j][i][4 * qq + q], sm[i] * cfv[q], cbv[q]);
-          if constexpr (F32) {
-            *(float4*)((float*)g.out + m * g.N + n0) = make_float4(y[0], y[1], y[2], y[3]);
-          } else {
-            u32x2 w;
-            w.x = pack_bf16x2(y[0], y[1]);
-            w.y = pack_bf16x2(y[2], y[3]);
-            *(u32x2*)((uint16_t*)g.out + m * g.N + n0) = w;
+          for (int i = 0; i < WM; ++i) {
+            const long long m = m_base + 32 * i + r32;
+            if (m >= g.M) continue;
+            const float y = act_fn<ACT>(__builtin_fmaf(acc[j][i][4 * qq + q], sm[i] * cf, cb));
+            if (f32_out) ((float*)g.out)[m * g.N + n] = y;
+            else ((uint16_t*)g.out)[m * g.N + n] = f32_to_bf16_rne(y);
           }
         }
       }
     }
   };
-  // Whole tile inside a bf16 output with 16-byte aligned rows: the tile is
-  // staged in LDS (over the decode tables, which the K loop no longer needs)
-  // and written out row by row, 16 bytes per lane, so each output row of the
-  // tile leaves as whole cache lines instead of 16-byte pieces of 32 rows.
-  // The condition is the same for every wave of the workgroup.
-  const bool staged = !f32_out && (g.N & 7) == 0 && ((uintptr_t)g.out & 15) == 0 &&
-                      (long long)(tm + 1) * TM <= g.M && (long long)(tn + 1) * TN <= g.N;
-  if (staged) {
-    constexpr int kRow = TN * 2 + 16;  // padded LDS row: 2-way bank conflicts at most
-    __syncthreads();                   // every wave is done with the tables
-    const int lm = wm * (TM / 2) + r32, ln = wn * (TN / 2) + 4 * half;
-#pragma unroll
-    for (int j = 0; j < WN; ++j) {
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const float4 cf = *(const float4*)(wr + 32 * j + 8 * qq);
-        const float4 cb = *(const float4*)(wb + 32 * j + 8 * qq);
-        const float cfv[4] = {cf.x, cf.y, cf.z, cf.w}, cbv[4] = {cb.x, cb.y, cb.z, cb.w};
-#pragma unroll
-        for (int i = 0; i < WM; ++i) {
-          float y[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) y[q] = __builtin_fmaf(acc[j][i][4 * qq + q], sm[i] * cfv[q], cbv[q]);
-          u32x2 w;
-          w.x = pack_bf16x2(y[0], y[1]);
-          w.y = pack_bf16x2(y[2], y[3]);
-          *(u32x2*)(smem + (lm + 32 * i) * kRow + (ln + 32 * j + 8 * qq) * 2) = w;
-        }
-      }
-    }
-    __syncthreads();
-    constexpr int kChunks = TN * 2 / 16;  // 16-byte pieces per tile row
-    char* const out0 = (char*)g.out + ((long long)tm * TM * g.N + (long long)tn * TN) * 2;
-#pragma unroll 4
-    for (int q = t; q < TM * kChunks; q += 256) {
-      const int row = q / kChunks, c = q - row * kChunks;
-      const u32x4 v = *(const u32x4*)(smem + row * kRow + c * 16);
-      *(u32x4*)(out0 + (long long)row * g.N * 2 + c * 16) = v;
-    }
-    return;
-  }
-  if (fast) {
-    if (f32_out) epi(std::true_type{});
-    else epi(std::false_type{});
-    return;
-  }
-#pragma unroll
-  for (int j = 0; j < WN; ++j) {
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const long long n = n_base + 32 * j + 8 * qq + 4 * half + q;
-        if (n >= g.N) continue;
-        const float cf = wr[32 * j + 8 * qq + q], cb = wb[32 * j + 8 * qq + q];
-#pragma unroll
-        for (int i = 0; i < WM; ++i) {
-          const long long m = m_base + 32 * i + r32;
-          if (m >= g.M) continue;
-          const float y = __builtin_fmaf(acc[j][i][4 * qq + q], sm[i] * cf, cb);
-          if (f32_out) ((float*)g.out)[m * g.N + n] = y;
-          else ((uint16_t*)g.out)[m * g.N + n] = f32_to_bf16_rne(y);
-        }
-      }
-    }
-  }
+  if (g.act == ORBIT_ACT_GELU) finish(std::integral_constant<int, ORBIT_ACT_GELU>{});
+  else finish(std::integral_constant<int, ORBIT_ACT_NONE>{});
 }
 
 template <int KIND, class OpA, class OpB, int WM, int WN>

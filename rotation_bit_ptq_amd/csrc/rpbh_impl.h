@@ -598,6 +598,7 @@ __device__ __forceinline__ void lds_addresses(const RowArgs& a, const uint32_t* 
 // 16 T); LT < 0: consecutive gather with cross-lane butterfly stages.
 template <typename InT, int MODE, int BITS, int R, int LT>
 __global__ __launch_bounds__(256) void rows_kernel(RowArgs a) {
+  static_assert(R > 0, "rows longer than 4096 coordinates take long_rows_kernel");
   extern __shared__ __align__(16) char smem[];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -717,58 +718,116 @@ __global__ __launch_bounds__(256) void rows_kernel(RowArgs a) {
       if (MODE == kAct && a.xrot_f32) emit_all(std::true_type{});
       else emit_all(std::false_type{});
     }
-  } else {
-    if constexpr (kQuant) {
-      build_grid(a, smem);
-      __syncthreads();
-    }
-    const int nchunk = a.d * (int)sizeof(InT) / 16;
-    const uint32_t negoff = (uint32_t)a.d * (uint32_t)sizeof(InT);
-    const uint32_t flip = sizeof(InT) == 2 ? 0x80008000u : 0x80000000u;
-    for (; row < a.rows; row += stride) {
-      const u32x4* src = (const u32x4*)((const char*)a.in + (size_t)row * a.d * sizeof(InT));
-      for (int ch = lane; ch < nchunk; ch += kWave) {
-        u32x4 x = __builtin_nontemporal_load(src + ch);
-        *(u32x4*)(smem + wbuf + ch * 16) = x;
-        *(u32x4*)(smem + wbuf + negoff + ch * 16) = x ^ flip;
-      }
-      wave_lds_sync();
-      float ss = 0.0f, alpha = 0.0f;
-      for (int pass = kQuant ? 0 : 1; pass < 2; ++pass) {
-        for (int r = 0; r < a.nrounds; ++r) {
-          const int slot = r * kWave + lane;
-          uint32_t addr[kSlot];
-          float v[kSlot];
-          if constexpr (LT >= 0) {
-            tr_addresses<InT, LT>(a, slot, wbuf, addr);
-            tr_rotate<InT, LT>(smem, scr, addr, v, lane);
-          } else {
-            slot_addresses<InT>(a, slot, wbuf, addr);
-            gather_h16<InT>(smem, addr, v);
-            lane_stages(v, lane, nstages);
-          }
-          if (slot < a.nslots) {
-            if (pass == 0) {
-#pragma unroll
-              for (int i = 0; i < kSlot; ++i) ss = __builtin_fmaf(v[i], v[i], ss);
-            } else {
-              if (MODE == kAct && a.xrot_f32) emit_slot<MODE, BITS, true>(a, row, slot, lane, v, alpha, smem);
-              else emit_slot<MODE, BITS>(a, row, slot, lane, v, alpha, smem);
-            }
-          }
-        }
-        if (pass == 0) {
-          ss = wave_sum(ss);
-          alpha = row_alpha<MODE>(a, ss, row, lane);
-        }
-      }
-      wave_lds_sync();
-    }
   }
+}
+
+// Rows longer than 4096 coordinates: one workgroup of four waves per row.
+// The row lands once in a shared LDS buffer (as x and -x), its norm comes
+// from the loaded values through a fixed-order workgroup reduction, and the
+// rounds of 1024 coordinates are split across the waves; the next row's
+// loads are in flight meanwhile.  One pass over the row.
+template <typename InT, int MODE, int BITS, int LT>
+__global__ __launch_bounds__(256) void long_rows_kernel(RowArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  constexpr bool kQuant = (MODE == kAct || MODE == kWeight);
+  constexpr int kPer = ORBIT_MAX_D * (int)sizeof(InT) / 16 / 256;  // 16-byte chunks per thread
+  const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
+  float* const red = (float*)(smem + a.grid_bytes);         // four wave sums
+  const uint32_t rbuf = (uint32_t)a.grid_bytes + 16u;        // the row, x then -x
+  uint32_t scr = 0;
+  if constexpr (LT >= 0) scr = rbuf + (uint32_t)a.row_bytes + (uint32_t)(wave * TrShape<LT>::kScratchBytes);
+  const int nchunk = a.d * (int)sizeof(InT) / 16;
+  const uint32_t negoff = (uint32_t)a.d * (uint32_t)sizeof(InT);
+  const uint32_t flip = sizeof(InT) == 2 ? 0x80008000u : 0x80000000u;
+  const int nstages = a.log2h - 4;
+  if constexpr (kQuant) build_grid(a, smem);  // visible after the first barrier below
+
+  u32x4 pre[kPer];
+  auto load = [&](long long rr) {
+    const u32x4* src = (const u32x4*)((const char*)a.in + (size_t)rr * a.d * sizeof(InT));
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int ch = t + 256 * i;
+      if (ch < nchunk) pre[i] = __builtin_nontemporal_load(src + ch);
+    }
+  };
+  long long row = blockIdx.x;
+  if (row < a.rows) load(row);
+  for (; row < a.rows; row += gridDim.x) {
+    float ssx = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int ch = t + 256 * i;
+      if (ch < nchunk) {
+        if constexpr (kQuant) ssx = RowRegs<InT, 1>::chunk_sumsq(pre[i], ssx);
+        *(u32x4*)(smem + rbuf + ch * 16) = pre[i];
+        *(u32x4*)(smem + rbuf + negoff + ch * 16) = pre[i] ^ flip;
+      }
+    }
+    if (row + gridDim.x < a.rows) load(row + gridDim.x);
+    if constexpr (kQuant) {
+      const float ws = wave_sum(ssx);
+      if (lane == 0) red[wave] = ws;
+    }
+    __syncthreads();  // the row and the wave sums are in LDS
+    float alpha = 0.0f;
+    if constexpr (kQuant) alpha = row_alpha<MODE, true>(a, (red[0] + red[1]) + (red[2] + red[3]), row, t);
+    for (int r = wave; r < a.nrounds; r += 4) {
+      const int slot = r * kWave + lane;
+      uint32_t addr[kSlot];
+      float v[kSlot];
+      if (a.gather) {  // uniform
+        const u32x4* src = (const u32x4*)(a.gather + r * 1024 + lane * kSlot);
+        const u32x4 g0 = src[0], g1 = src[1];
+        const uint32_t w[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+        for (int e = 0; e < kSlot; ++e)
+          addr[e] = rbuf + ((w[e >> 1] >> (16 * (e & 1))) & 0xffffu) * (uint32_t)sizeof(InT);
+      } else if constexpr (LT >= 0) {
+        tr_addresses<InT, LT>(a, slot, rbuf, addr);
+      } else {
+        slot_addresses<InT>(a, slot, rbuf, addr);
+      }
+      if constexpr (LT >= 0) {
+        tr_rotate<InT, LT>(smem, scr, addr, v, lane);
+      } else {
+        gather_h16<InT>(smem, addr, v);
+        lane_stages(v, lane, nstages);
+      }
+      if (slot < a.nslots) {
+        if (MODE == kAct && a.xrot_f32) emit_slot<MODE, BITS, true>(a, row, slot, lane, v, alpha, smem);
+        else emit_slot<MODE, BITS>(a, row, slot, lane, v, alpha, smem);
+      }
+    }
+    __syncthreads();  // every wave has gathered before the next row lands
+  }
+}
+
+template <typename InT, int MODE, int BITS, int LT>
+hipError_t launch_long(RowArgs a, hipStream_t stream) {
+  DeviceInfo di;
+  hipError_t e = device_info(&di);
+  if (e != hipSuccess) return e;
+  if (a.d > ORBIT_MAX_D) return hipErrorInvalidValue;
+  int lds = a.grid_bytes + 16 + a.row_bytes;
+  if constexpr (LT >= 0) lds += 4 * TrShape<LT>::kScratchBytes;
+  if (lds > di.max_lds) return hipErrorInvalidValue;
+  auto kern = long_rows_kernel<InT, MODE, BITS, LT>;
+  static LaunchCache cache;
+  int per_cu = 1;
+  e = prepare_launch(cache, (const void*)kern, 256, lds, &per_cu);
+  if (e != hipSuccess) return e;
+  const long long cap = (long long)di.n_cu * per_cu;
+  const int blocks = (int)(a.rows < cap ? a.rows : cap);
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), lds, stream, a);
+  return hipGetLastError();
 }
 
 template <typename InT, int MODE, int BITS, int R, int LT>
 hipError_t launch_typed(RowArgs a, hipStream_t stream) {
+  if constexpr (R == 0) {
+    return launch_long<InT, MODE, BITS, LT>(a, stream);
+  } else {
   DeviceInfo di;
   hipError_t e = device_info(&di);
   if (e != hipSuccess) return e;
@@ -791,9 +850,11 @@ hipError_t launch_typed(RowArgs a, hipStream_t stream) {
   const int blocks = (int)(need < cap ? need : cap);
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(waves * kWave), lds, stream, a);
   return hipGetLastError();
+  }
 }
 
-// Register-resident rounds for a row of d coordinates (0 = two-pass path).
+// Register-resident rounds for a row of d coordinates (0 = the long-row
+// kernel, one workgroup per row).
 inline int rounds_for(int d) {
   const int r = (d / kSlot + kWave - 1) / kWave;
   return r <= kMaxCachedRounds ? r : 0;

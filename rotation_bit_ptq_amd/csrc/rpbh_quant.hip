@@ -65,9 +65,9 @@ hipError_t launch_rows(const RowJob& job, hipStream_t stream) {
   // bf16 rows with h = 64, 128 or 256: transposed-gather kernels
   const bool tr_order = job.h == 64 || job.h == 128 || job.h == 256;
   const bool fast = bf16 && tr_order && (!quant || job.bits != 1);
-  // the gather plan serves the register-resident kernels (d <= 4096) whose
-  // gather order it was built in (transposed exactly when h allows it)
-  if (job.gather && job.d <= 4096 && fast == tr_order) a.gather = job.gather;
+  // the gather plan serves the kernels whose gather order it was built in
+  // (transposed exactly when h allows it)
+  if (job.gather && fast == tr_order) a.gather = job.gather;
   if (fast) {
     const int lt = job.h == 64 ? 2 : (job.h == 128 ? 3 : 4);
     if (job.mode == RowMode::kActQuant) {
@@ -120,7 +120,7 @@ template <int LT>
 __global__ __launch_bounds__(256) void gather_plan_kernel(int d, const int32_t* perm,
                                                           const uint32_t* sign_bits, uint16_t* out) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= kGatherLen) return;
+  if (i >= gather_len(d)) return;
   const int r = i >> 10, l = (i >> 4) & 63, e = i & 15;
   const int slot = r * rows::kWave + l;
   uint32_t v = 0;
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(256) void gather_plan_kernel(int d, const int32_t* 
 
 hipError_t launch_gather_plan(int d, int h, const int32_t* perm, const uint32_t* sign_bits,
                               uint16_t* out, hipStream_t stream) {
-  const dim3 grid(kGatherLen / 256), block(256);
+  const dim3 grid(gather_len(d) / 256), block(256);
   if (h == 64) hipLaunchKernelGGL(gather_plan_kernel<2>, grid, block, 0, stream, d, perm, sign_bits, out);
   else if (h == 128) hipLaunchKernelGGL(gather_plan_kernel<3>, grid, block, 0, stream, d, perm, sign_bits, out);
   else if (h == 256) hipLaunchKernelGGL(gather_plan_kernel<4>, grid, block, 0, stream, d, perm, sign_bits, out);

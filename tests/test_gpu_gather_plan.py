@@ -16,12 +16,12 @@ from parity import to_dev
 pytestmark = pytest.mark.gpu
 
 
-def _plan_reference(perm, signs, h):
+def _plan_reference(perm, signs, h, rounds=4):
     """The documented layout: entry r*1024 + l*16 + e."""
     d = perm.shape[0]
-    out = np.zeros(4096, dtype=np.int64)
+    out = np.zeros(1024 * rounds, dtype=np.int64)
     T = h // 16 if h in (64, 128, 256) else None
-    for r in range(4):
+    for r in range(rounds):
         for lane in range(64):
             s = 64 * r + lane
             if s >= d // 16:
@@ -47,10 +47,14 @@ def test_plan_layout(gpu_lib, d, h):
     assert np.array_equal(got, _plan_reference(perm, signs, h))
 
 
-def test_no_plan_for_long_rows(gpu_lib):
-    perm, signs = synth.rotation_params(8192, 3)
-    rot = gpu_lib.Rotation(perm, signs, 256)
-    assert rot.gather is None
+def test_plan_for_long_rows(gpu_lib):
+    d, h = 12288, 256
+    perm, signs = synth.rotation_params(d, 3)
+    rot = gpu_lib.Rotation(perm, signs, h)
+    torch.cuda.synchronize()
+    got = rot.gather.cpu().numpy().view(np.uint16).astype(np.int64)
+    assert got.shape == (12288,)
+    assert np.array_equal(got, _plan_reference(perm, signs, h, rounds=12))
 
 
 @pytest.mark.parametrize("cfg,K,h,bits,f32", [

@@ -124,3 +124,17 @@ def test_permutation_gives_variance_one_over_d():
 def test_haar_is_orthogonal():
     Q = oracle.haar_matrix(96, 5)
     np.testing.assert_allclose(Q @ Q.T, np.eye(96), atol=1e-12)
+
+
+def test_down_permutation_folds_into_up_rows():
+    """Pi_down GELU(z) with pi applied to z's rows first is the block
+    rotation alone: blkdiag(H D) GELU(P_pi z) = Pi_down GELU(z) (GELU acts
+    elementwise, so it commutes with the permutation)."""
+    g = np.random.default_rng(11)
+    d, h = 512, 128
+    perm = g.permutation(d)
+    signs = g.choice([-1.0, 1.0], size=d)
+    Z = g.standard_normal((6, d)) * 2.0
+    full = oracle.rpbh_rotate(oracle.gelu_erf(Z), perm, signs, h)
+    folded = oracle.block_rht_rotate(oracle.gelu_erf(Z[:, perm]), signs, h)
+    assert np.allclose(full, folded, rtol=0, atol=1e-12)
