@@ -18,6 +18,8 @@ It is written as a plain, slow, direct reading of the pages, in float64:
 * Int8 rotated-weight article (cloud.baidu.com, "量化旋转压缩主模型技术解析",
   section 4 "How it works"): rotate -> per-group scale -> round -> store;
   at load time dequantize -> inverse-rotate -> ordinary layer forward.
+  Its 4-bit sibling (``int4``) stands for the INT4 projections the OrbitQuant
+  page's Experiments section favours in its ablations.
 
 Readings where the pages are silent (each is listed in the design doc):
 Hadamard matrices are Sylvester-ordered and orthonormal (H_h / sqrt(h));
@@ -26,7 +28,9 @@ the codebook is stored in N(0,1) units (the N(0,1/d) codebook is it divided
 by sqrt(d)); the quantizer returns idx = #{j : t_j < u} for the sorted
 midpoint thresholds t_j; index k of a row takes bits [k*b, (k+1)*b) of the
 row's LSB-first byte stream; int8 uses the symmetric range [-127, 127], a
-per-(row, group of 128) fp16 scale fp16(max|w'| / 127) and round half to even.
+per-(row, group of 128) fp16 scale fp16(max|w'| / 127) and round half to even;
+int4 is the same recipe with [-7, 7] and fp16(max|w'| / 7), codes stored as
+two's-complement nibbles, low nibble first.
 
 Where a floating-point value decides an integer (a codebook index, a bf16 row
 norm, an fp16 scale, an int8 code), the decision is taken in float32, the
@@ -51,6 +55,7 @@ from .orbit import (quantize_codes, boundary_band, pack_indices, unpack_indices,
                     pack_weights, quant_act, qlinear_codes, qlinear_unquantized,
                     gelu_erf)
 from .int8 import int8_pack, int8_dequant, int8_linear
+from .int4 import int4_pack, int4_dequant, int4_linear, pack_nibbles, unpack_nibbles
 
 __all__ = [
     "bf16_bits_to_f64", "f64_to_bf16_bits", "f16_bits_to_f64", "f64_to_f16_bits",
@@ -59,5 +64,6 @@ __all__ = [
     "lloyd_max_gaussian", "codebook", "quantize_codes", "boundary_band",
     "pack_indices", "unpack_indices", "pack_weights", "quant_act",
     "qlinear_codes", "qlinear_unquantized", "gelu_erf", "int8_pack",
-    "int8_dequant", "int8_linear",
+    "int8_dequant", "int8_linear", "int4_pack", "int4_dequant", "int4_linear",
+    "pack_nibbles", "unpack_nibbles",
 ]
