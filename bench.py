@@ -179,6 +179,52 @@ def mlp_pair(rbp, torch, dev, stream, n=3):
             "fused_tflops": round(flops / tf / 1e6, 1), "unfused_tflops": round(flops / tu / 1e6, 1)}
 
 
+def weight_only(rbp, torch, dev, stream, n=10):
+    """The per-group rotated weight-only paths, int8 and its int4 sibling,
+    on two shapes: the int8 workload (16384 tokens, 4096 -> 4096, h = 128;
+    compute-bound) and an AdaLN-style projection (16 conditioning vectors,
+    3072 -> 18432; bound by the weight stream).  Per shape: the rotation of
+    the activations (bf16 -> fp16) and each GEMM in microseconds per launch,
+    with TFLOP/s and the weight bytes streamed per microsecond (GB/s)."""
+    import synth
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        b.synchronize()
+        return a.elapsed_time(b) * 1e3 / n
+
+    res = {}
+    for name, (M, K, N) in (("int8_workload_16384x4096x4096", (16384, 4096, 4096)),
+                            ("adaln_16x3072x18432", (16, 3072, 18432))):
+        perm, signs = synth.rotation_params(K, 7)
+        g = torch.Generator(device=dev).manual_seed(5)
+        X = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
+        W = (torch.randn((N, K), generator=g, device=dev) / K ** 0.5).to(torch.bfloat16)
+        rot = rbp.Rotation(perm, signs, 128)
+        q8, s8 = rbp.int8_pack_weights(rot, W, 128)
+        q4, s4 = rbp.int4_pack_weights(rot, W, 128)
+        xr = rbp.rotate(rot, X, out_dtype=torch.float16)
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        t_rot = timed(lambda: rbp.rotate(rot, X, out_dtype=torch.float16, out=xr))
+        t8 = timed(lambda: rbp.int8_linear(xr, q8, s8, 128, out=out))
+        t4 = timed(lambda: rbp.int4_linear(xr, q4, s4, 128, out=out))
+        flops = 2.0 * M * K * N
+        res[name] = {"rotate_us": round(t_rot, 2),
+                     "w8a16_us": round(t8, 2), "w4a16_us": round(t4, 2),
+                     "w8a16_tflops": round(flops / t8 / 1e6, 1),
+                     "w4a16_tflops": round(flops / t4 / 1e6, 1),
+                     "w8_weight_gbps": round(N * K / t8 / 1e3, 1),
+                     "w4_weight_gbps": round(N * K / 2 / t4 / 1e3, 1)}
+    return res
+
+
 def source_digest(files):
     """sha256 over the kernel sources a traffic measurement was taken with."""
     import hashlib
@@ -351,6 +397,7 @@ def main():
     }
     line["rotation_ablation"] = rotation_ablation(rbp, torch, dev, stream)
     line["mlp_pair"] = mlp_pair(rbp, torch, dev, stream)
+    line["weight_only"] = weight_only(rbp, torch, dev, stream)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(line), flush=True)

@@ -216,6 +216,33 @@ orbit_status orbit_int8_linear(const void *Xrot, orbit_dtype xrot_dtype, int64_t
                                int64_t N, const void *bias, orbit_dtype bias_dtype,
                                void *out, orbit_dtype out_dtype, hipStream_t stream);
 
+/* Int4 rotated weight packer: the 4-bit sibling of orbit_int8_pack_weights
+ * (int8 article, section 4 pack_weight, with the INT4 projections of the
+ * OrbitQuant page's Experiments section): W' = W Pi^T; per row and group of
+ * `group` consecutive columns scale = fp16(max|w'| / 7) (float32 division,
+ * nearest even); q = clamp(round_half_even(w' / scale), -7, 7), q = 0 where
+ * scale = 0.  W: device [N, K] F32 or BF16; q_out: device uint8 [N, K/2],
+ * two's-complement nibbles, code 2j in the low nibble of byte j, code 2j+1
+ * in the high nibble; scale_f16_out: device uint16 [N, K/group] (fp16 bits).
+ * group a multiple of 16 dividing K, group <= 1024; q_out 16-byte aligned.
+ * Errors as orbit_int8_pack_weights. */
+orbit_status orbit_int4_pack_weights(const orbit_rpbh *rot, const void *W, orbit_dtype w_dtype,
+                                     int64_t N, int64_t K, int32_t group,
+                                     uint8_t *q_out, uint16_t *scale_f16_out,
+                                     hipStream_t stream);
+
+/* Int4 weight-only GEMM on rotated activations, the 4-bit sibling of
+ * orbit_int8_linear: out[m, n] = sum_k Xrot[m,k] * q[n,k] * scale[n, k/group]
+ * (+ bias[n]).  Xrot: device [M, K] F16; q: device uint8 [N, K/2] in the
+ * layout orbit_int4_pack_weights writes; scale_f16: device uint16
+ * [N, K/group]; group == 128; K % 128 == 0; out: device [M, N], F32 or BF16.
+ * Weights are decoded to fp16 (q times scale, one rounding) and multiplied
+ * on fp16 matrix cores with fp32 accumulation.  Errors as orbit_int8_linear. */
+orbit_status orbit_int4_linear(const void *Xrot, orbit_dtype xrot_dtype, int64_t M, int64_t K,
+                               const uint8_t *q, const uint16_t *scale_f16, int32_t group,
+                               int64_t N, const void *bias, orbit_dtype bias_dtype,
+                               void *out, orbit_dtype out_dtype, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

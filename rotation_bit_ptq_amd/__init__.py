@@ -13,7 +13,7 @@ rotation Pi = blkdiag(H_h D_i) P_pi is absorbed offline into the weights
 applied online to activations (x' = Pi x, split into ||x'|| and a coded unit
 direction); the product of the two coded factors approximates W x with no
 inverse rotation.  Also: the int8 per-group rotated weight-only path of the
-int8 article (section 4).
+int8 article (section 4) and its 4-bit sibling (int4 codes, two per byte).
 """
 from __future__ import annotations
 
@@ -26,6 +26,7 @@ import torch
 __all__ = [
     "OrbitError", "Codebook", "Rotation", "fit_codebook", "pack_weights",
     "quant_act", "qlinear", "rotate", "int8_pack_weights", "int8_linear",
+    "int4_pack_weights", "int4_linear",
     "packed_row_bytes", "LIB_PATH",
 ]
 
@@ -72,7 +73,10 @@ def _load():
                                ctypes.c_int, ctypes.c_int, P], ctypes.c_int),
         "orbit_rotate": ([P, P, ctypes.c_int, I64, I64, P, ctypes.c_int, P], ctypes.c_int),
         "orbit_int8_pack_weights": ([P, P, ctypes.c_int, I64, I64, I32, P, P, P], ctypes.c_int),
+        "orbit_int4_pack_weights": ([P, P, ctypes.c_int, I64, I64, I32, P, P, P], ctypes.c_int),
         "orbit_int8_linear": ([P, ctypes.c_int, I64, I64, P, P, I32, I64, P, ctypes.c_int,
+                               P, ctypes.c_int, P], ctypes.c_int),
+        "orbit_int4_linear": ([P, ctypes.c_int, I64, I64, P, P, I32, I64, P, ctypes.c_int,
                                P, ctypes.c_int, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
@@ -255,4 +259,34 @@ def int8_linear(xrot: torch.Tensor, q: torch.Tensor, scale: torch.Tensor, group:
     _check(lib.orbit_int8_linear(_ptr(xrot), _DT[xrot.dtype], M, K, _ptr(q), _ptr(scale), group,
                                  N, _ptr(bias), bias_dt, _ptr(out), _DT[out.dtype],
                                  _stream(xrot.device)), "orbit_int8_linear")
+    return out
+
+
+def int4_pack_weights(rot: Rotation, W: torch.Tensor, group: int = 128):
+    """Offline int4: (q uint8 [N, K/2] two codes per byte, scales fp16 [N, K/group])."""
+    _dev(W, "W")
+    N, K = W.shape
+    q = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
+    sc = torch.empty((N, K // group), dtype=torch.float16, device=W.device)
+    _check(lib.orbit_int4_pack_weights(ctypes.byref(rot.struct), _ptr(W), _DT[W.dtype], N, K,
+                                       group, _ptr(q), _ptr(sc), _stream(W.device)),
+           "orbit_int4_pack_weights")
+    return q, sc
+
+
+def int4_linear(xrot: torch.Tensor, q: torch.Tensor, scale: torch.Tensor, group: int = 128,
+                bias=None, out_dtype=torch.bfloat16, out=None):
+    """out = x' (q * scale)^T (+ bias), x' = Pi x in fp16, q int4 two per byte."""
+    for t, n in ((xrot, "xrot"), (q, "q"), (scale, "scale")):
+        _dev(t, n)
+    M, K = xrot.shape
+    N = q.shape[0]
+    if q.shape[1] * 2 != K:
+        raise ValueError("q must be [N, K/2]")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=xrot.device)
+    bias_dt = _DT[bias.dtype] if bias is not None else F32
+    _check(lib.orbit_int4_linear(_ptr(xrot), _DT[xrot.dtype], M, K, _ptr(q), _ptr(scale), group,
+                                 N, _ptr(bias), bias_dt, _ptr(out), _DT[out.dtype],
+                                 _stream(xrot.device)), "orbit_int4_linear")
     return out

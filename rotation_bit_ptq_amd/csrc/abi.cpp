@@ -82,6 +82,63 @@ orbit_status check_rows_in(const void* in, orbit_dtype dt, int64_t rows) {
   return ORBIT_OK;
 }
 
+// Rotate + per-group pack of weight rows (int8 or int4 codes).
+orbit_status group_pack(orbit::RowMode mode, const orbit_rpbh* rot, const void* W,
+                        orbit_dtype w_dtype, int64_t N, int64_t K, int32_t group, int8_t* q_out,
+                        uint16_t* scale_f16_out, hipStream_t stream) {
+  orbit_status st = check_rot(rot, K);
+  if (st != ORBIT_OK) return st;
+  if ((st = check_rows_in(W, w_dtype, N)) != ORBIT_OK) return st;
+  if (!pow2(group) || group < 16 || group > 1024 || K % group) return ORBIT_E_SHAPE;
+  if (N > 0 && (!q_out || !scale_f16_out || !aligned16(q_out))) return ORBIT_E_ARG;
+  orbit::RowJob job = {};
+  job.mode = mode;
+  job.in_dtype = w_dtype;
+  job.rows = N;
+  job.d = (int)K;
+  job.h = rot->h;
+  job.perm = rot->perm;
+  job.gather = rot->gather;
+  job.sign_bits = rot->sign_bits;
+  job.in = W;
+  job.group = group;
+  job.q_out = q_out;
+  job.scale_out = scale_f16_out;
+  return hip_status(orbit::launch_rows(job, stream));
+}
+
+// fp16 rotated activations x int8 (kind 1) or int4 (kind 2) weights.
+orbit_status group_linear(int kind, const void* Xrot, orbit_dtype xrot_dtype, int64_t M, int64_t K,
+                          const uint8_t* q, const uint16_t* scale_f16, int32_t group, int64_t N,
+                          const void* bias, orbit_dtype bias_dtype, void* out,
+                          orbit_dtype out_dtype, hipStream_t stream) {
+  if (xrot_dtype != ORBIT_F16) return ORBIT_E_DTYPE;
+  if (out_dtype != ORBIT_F32 && out_dtype != ORBIT_BF16) return ORBIT_E_DTYPE;
+  if (bias && bias_dtype != ORBIT_F32 && bias_dtype != ORBIT_BF16) return ORBIT_E_DTYPE;
+  if (group != 128) return ORBIT_E_UNSUPPORTED;
+  if (M < 0 || N < 0 || K < 128 || K > 65536 || K % 128) return ORBIT_E_SHAPE;
+  if (M > 0 && N > 0) {
+    if (!Xrot || !q || !scale_f16 || !out) return ORBIT_E_ARG;
+    if (!aligned16(Xrot) || !aligned16(q) || !aligned16(out)) return ORBIT_E_ARG;
+  }
+  const int64_t ldb = kind == 2 ? K / 2 : K;
+  if (M * K * 2 >= (1LL << 31) || N * ldb >= (1LL << 31)) return ORBIT_E_UNSUPPORTED;
+  orbit::GemmJob job = {};
+  job.kind = kind;
+  job.M = M;
+  job.N = N;
+  job.K = K;
+  job.a = (const uint8_t*)Xrot;
+  job.b = q;
+  job.scale_f16 = scale_f16;
+  job.group = group;
+  job.bias = bias;
+  job.bias_dtype = bias_dtype;
+  job.out = out;
+  job.out_dtype = out_dtype;
+  return hip_status(orbit::launch_gemm(job, stream));
+}
+
 }  // namespace
 
 namespace orbit {
@@ -251,25 +308,31 @@ orbit_status orbit_rotate(const orbit_rpbh* rot, const void* X, orbit_dtype x_dt
 orbit_status orbit_int8_pack_weights(const orbit_rpbh* rot, const void* W, orbit_dtype w_dtype,
                                      int64_t N, int64_t K, int32_t group, int8_t* q_out,
                                      uint16_t* scale_f16_out, hipStream_t stream) {
-  orbit_status st = check_rot(rot, K);
-  if (st != ORBIT_OK) return st;
-  if ((st = check_rows_in(W, w_dtype, N)) != ORBIT_OK) return st;
-  if (!pow2(group) || group < 16 || group > 1024 || K % group) return ORBIT_E_SHAPE;
-  if (N > 0 && (!q_out || !scale_f16_out || !aligned16(q_out))) return ORBIT_E_ARG;
-  orbit::RowJob job = {};
-  job.mode = orbit::RowMode::kInt8Pack;
-  job.in_dtype = w_dtype;
-  job.rows = N;
-  job.d = (int)K;
-  job.h = rot->h;
-  job.perm = rot->perm;
-  job.gather = rot->gather;
-  job.sign_bits = rot->sign_bits;
-  job.in = W;
-  job.group = group;
-  job.q_out = q_out;
-  job.scale_out = scale_f16_out;
-  return hip_status(orbit::launch_rows(job, stream));
+  return group_pack(orbit::RowMode::kInt8Pack, rot, W, w_dtype, N, K, group, q_out,
+                    scale_f16_out, stream);
+}
+
+orbit_status orbit_int4_pack_weights(const orbit_rpbh* rot, const void* W, orbit_dtype w_dtype,
+                                     int64_t N, int64_t K, int32_t group, uint8_t* q_out,
+                                     uint16_t* scale_f16_out, hipStream_t stream) {
+  return group_pack(orbit::RowMode::kInt4Pack, rot, W, w_dtype, N, K, group, (int8_t*)q_out,
+                    scale_f16_out, stream);
+}
+
+orbit_status orbit_int4_linear(const void* Xrot, orbit_dtype xrot_dtype, int64_t M, int64_t K,
+                               const uint8_t* q, const uint16_t* scale_f16, int32_t group,
+                               int64_t N, const void* bias, orbit_dtype bias_dtype, void* out,
+                               orbit_dtype out_dtype, hipStream_t stream) {
+  return group_linear(2, Xrot, xrot_dtype, M, K, q, scale_f16, group, N, bias, bias_dtype, out,
+                      out_dtype, stream);
+}
+
+orbit_status orbit_int8_linear(const void* Xrot, orbit_dtype xrot_dtype, int64_t M, int64_t K,
+                               const int8_t* q, const uint16_t* scale_f16, int32_t group, int64_t N,
+                               const void* bias, orbit_dtype bias_dtype, void* out,
+                               orbit_dtype out_dtype, hipStream_t stream) {
+  return group_linear(1, Xrot, xrot_dtype, M, K, (const uint8_t*)q, scale_f16, group, N, bias,
+                      bias_dtype, out, out_dtype, stream);
 }
 
 orbit_status orbit_qlinear_act(const uint8_t* idx_a, const float* s, const orbit_codebook* ca,
@@ -319,36 +382,6 @@ orbit_status orbit_qlinear(const uint8_t* idx_a, const float* s, const orbit_cod
                            void* out, orbit_dtype out_dtype, hipStream_t stream) {
   return orbit_qlinear_act(idx_a, s, ca, idx_w, r_bf16, cw, bias, bias_dtype, M, N, K, out,
                            out_dtype, ORBIT_ACT_NONE, stream);
-}
-
-orbit_status orbit_int8_linear(const void* Xrot, orbit_dtype xrot_dtype, int64_t M, int64_t K,
-                               const int8_t* q, const uint16_t* scale_f16, int32_t group, int64_t N,
-                               const void* bias, orbit_dtype bias_dtype, void* out,
-                               orbit_dtype out_dtype, hipStream_t stream) {
-  if (xrot_dtype != ORBIT_F16) return ORBIT_E_DTYPE;
-  if (out_dtype != ORBIT_F32 && out_dtype != ORBIT_BF16) return ORBIT_E_DTYPE;
-  if (bias && bias_dtype != ORBIT_F32 && bias_dtype != ORBIT_BF16) return ORBIT_E_DTYPE;
-  if (group != 128) return ORBIT_E_UNSUPPORTED;
-  if (M < 0 || N < 0 || K < 128 || K > 65536 || K % 128) return ORBIT_E_SHAPE;
-  if (M > 0 && N > 0) {
-    if (!Xrot || !q || !scale_f16 || !out) return ORBIT_E_ARG;
-    if (!aligned16(Xrot) || !aligned16(q) || !aligned16(out)) return ORBIT_E_ARG;
-  }
-  if (M * K * 2 >= (1LL << 31) || N * K >= (1LL << 31)) return ORBIT_E_UNSUPPORTED;
-  orbit::GemmJob job = {};
-  job.kind = 1;
-  job.M = M;
-  job.N = N;
-  job.K = K;
-  job.a = (const uint8_t*)Xrot;
-  job.b = (const uint8_t*)q;
-  job.scale_f16 = scale_f16;
-  job.group = group;
-  job.bias = bias;
-  job.bias_dtype = bias_dtype;
-  job.out = out;
-  job.out_dtype = out_dtype;
-  return hip_status(orbit::launch_gemm(job, stream));
 }
 
 }  // extern "C"

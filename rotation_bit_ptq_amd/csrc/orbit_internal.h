@@ -32,6 +32,7 @@ enum class RowMode : int {
   kWeightQuant = 1,  // r = ||w'|| (bf16), u = sqrt(d) w' / r
   kRotate = 2,       // x' only
   kInt8Pack = 3,     // per-group fp16 scale, int8 codes
+  kInt4Pack = 4,     // per-group fp16 scale, int4 codes (two per byte)
 };
 
 // Uniform-grid lookup that turns "count thresholds below u" into one table
@@ -65,7 +66,7 @@ struct RowJob {
   void* rot_out;            // rotate F16 output
   // int8 outputs
   int group;
-  int8_t* q_out;
+  int8_t* q_out;  // int8 codes, or int4 codes two per byte
   uint16_t* scale_out;
 };
 
@@ -83,16 +84,16 @@ hipError_t launch_gather_plan(int d, int h, const int32_t* perm, const uint32_t*
 // ---- decode GEMMs (qgemm.hip) ----------------------------------------------
 
 struct GemmJob {
-  int kind;  // 0: codebook x codebook, 1: fp16 x int8
+  int kind;  // 0: codebook x codebook, 1: fp16 x int8, 2: fp16 x int4
   int64_t M, N, K;
-  const uint8_t* a;        // kind 0: idx_a; kind 1: fp16 Xrot
-  const uint8_t* b;        // kind 0: idx_w; kind 1: int8 q
+  const uint8_t* a;        // kind 0: idx_a; kinds 1, 2: fp16 Xrot
+  const uint8_t* b;        // kind 0: idx_w; kind 1: int8 q; kind 2: int4 q
   int bits_a, bits_b;      // kind 0
   const float* cent_a;     // host, 2^bits_a
   const float* cent_b;     // host, 2^bits_b
   const float* s;          // kind 0: per-row scale of A (device)
   const uint16_t* r_bf16;  // kind 0: per-row scale of B (device, bf16)
-  const uint16_t* scale_f16;  // kind 1: group scales (device)
+  const uint16_t* scale_f16;  // kinds 1, 2: group scales (device)
   int group;
   const void* bias;
   int bias_dtype;

@@ -49,11 +49,11 @@ hipError_t launch_gemm(const GemmJob& job, hipStream_t stream) {
     return hipErrorInvalidValue;
   }
   g.lda = job.K * 2;
-  g.ldb = job.K;
+  g.ldb = job.kind == 2 ? job.K / 2 : job.K;
   g.groups_per_row = (int)(job.K / job.group);
   g.table_a_offset = 0;
   g.table_b_offset = 0;
-  return launch_int8(g, stream);
+  return job.kind == 2 ? launch_int4(g, stream) : launch_int8(g, stream);
 }
 
 }  // namespace orbit

@@ -249,6 +249,43 @@ struct I8Op {  // int8 weight rows with an fp16 scale for the chunk's group
   }
 };
 
+struct I4Op {  // int4 weight rows (two's-complement nibbles, low nibble
+               // first) with an fp16 scale for the chunk's group
+  static constexpr int kChunkK = 32;
+  static constexpr int kBytes = 8;  // 16 codes per lane per chunk
+  uint2 v;
+  uint32_t scale2;  // the group's fp16 scale in both halves
+  __device__ __forceinline__ void load(const uint8_t* p) { v = *(const uint2*)p; }
+  static __device__ __forceinline__ uint32_t lane_base(uint32_t, uint32_t) { return 0; }
+  __device__ __forceinline__ half8 decode(int s, uint32_t) const {
+    // codes 8 s .. 8 s + 7 of the lane's 16; q + 8 as an unsigned nibble u,
+    // spread one per byte in code order, then fp16 bits 0x6400 | u =
+    // 1024 + u exactly; subtracting 1032 gives q exactly; one multiply by
+    // the scale rounds once
+    const uint32_t w = (s ? v.y : v.x) ^ 0x88888888u;
+    const uint32_t even = w & 0x0f0f0f0fu;         // codes 0, 2, 4, 6
+    const uint32_t odd = (w >> 4) & 0x0f0f0f0fu;   // codes 1, 3, 5, 7
+    const uint32_t lo = __builtin_amdgcn_perm(odd, even, 0x05010400u);  // codes 0..3
+    const uint32_t hi = __builtin_amdgcn_perm(odd, even, 0x07030602u);  // codes 4..7
+    const uint32_t mag = 0x64646464u;
+    uint32_t h[4];
+    h[0] = __builtin_amdgcn_perm(mag, lo, 0x04010400u);
+    h[1] = __builtin_amdgcn_perm(mag, lo, 0x04030402u);
+    h[2] = __builtin_amdgcn_perm(mag, hi, 0x04010400u);
+    h[3] = __builtin_amdgcn_perm(mag, hi, 0x04030402u);
+    typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+    const half2v bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const half2v sc = __builtin_bit_cast(half2v, scale2);
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      half2v q = __builtin_bit_cast(half2v, h[i]) - bias;
+      o[i] = __builtin_bit_cast(uint32_t, q * sc);
+    }
+    return __builtin_bit_cast(half8, make_uint4(o[0], o[1], o[2], o[3]));
+  }
+};
+
 // two floats to packed bf16, round to nearest even (v_cvt_pk_bf16_f32);
 // NaN stays NaN
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -329,7 +366,7 @@ __device__ __forceinline__ void issue_schedule(std::integer_sequence<int, K...>)
   (issue_slot<NMF, NDS, NVA, NVM, K>(), ...);
 }
 
-// KIND 0: codebook x codebook; KIND 1: fp16 x int8 with group scales.
+// KIND 0: codebook x codebook; KIND 1: fp16 x int8 or int4 with group scales.
 // WM token blocks and WN weight blocks of 32 per wave.
 template <int KIND, class OpA, class OpB, int WM, int WN>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
@@ -779,6 +816,7 @@ hipError_t launch_codes_b(GemmArgs& g, int bb, hipStream_t stream, bool same);
   }
 
 hipError_t launch_int8(GemmArgs& g, hipStream_t stream);
+hipError_t launch_int4(GemmArgs& g, hipStream_t stream);
 
 }  // namespace qgemm
 }  // namespace orbit

@@ -85,7 +85,7 @@ struct RowArgs {
 };
 static_assert(sizeof(RowArgs) <= 4096, "kernel arguments must stay within 4 KB");
 
-enum Mode { kAct = 0, kWeight = 1, kRotF32 = 2, kRotF16 = 3, kInt8 = 4 };
+enum Mode { kAct = 0, kWeight = 1, kRotF32 = 2, kRotF16 = 3, kInt8 = 4, kInt4 = 5 };
 
 struct GridCell {
   float t;   // the threshold inside the cell, +inf if none
@@ -487,7 +487,10 @@ __device__ __forceinline__ void emit_slot(const RowArgs& a, long long row, int s
     uint4* o = (uint4*)(a.xrot_f16 + (size_t)row * d + slot * kSlot);
     o[0] = make_uint4(w[0], w[1], w[2], w[3]);
     o[1] = make_uint4(w[4], w[5], w[6], w[7]);
-  } else {  // kInt8: per-group symmetric scale, round half to even
+  } else {  // kInt8 / kInt4: per-group symmetric scale, round half to even
+    static_assert(MODE == kInt8 || MODE == kInt4, "unknown mode");
+    constexpr float kQmax = MODE == kInt8 ? 127.0f : 7.0f;
+    constexpr int kCodeBits = MODE == kInt8 ? 8 : 4;  // two's complement
     float w[kSlot];
     float amax = 0.0f;
 #pragma unroll
@@ -497,16 +500,19 @@ __device__ __forceinline__ void emit_slot(const RowArgs& a, long long row, int s
     }
     const int lanes = a.group / kSlot;  // lanes per group, a power of two <= 64
     amax = group_max(amax, lanes);
-    const uint16_t sbits = f32_to_f16_rne(amax / 127.0f);
+    const uint16_t sbits = f32_to_f16_rne(amax / kQmax);
     const float sc = (float)__builtin_bit_cast(_Float16, sbits);
     uint32_t q4[4] = {0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < kSlot; ++i) {
       float qf = 0.0f;
-      if (sc > 0.0f) qf = fminf(fmaxf(__builtin_rintf(w[i] / sc), -127.0f), 127.0f);
-      q4[i / 4] |= ((uint32_t)(int)qf & 0xffu) << (8 * (i % 4));
+      if (sc > 0.0f) qf = fminf(fmaxf(__builtin_rintf(w[i] / sc), -kQmax), kQmax);
+      constexpr int kPer = 32 / kCodeBits;
+      q4[i / kPer] |= ((uint32_t)(int)qf & ((1u << kCodeBits) - 1u)) << (kCodeBits * (i % kPer));
     }
-    *(uint4*)(a.q_out + (size_t)row * d + slot * kSlot) = make_uint4(q4[0], q4[1], q4[2], q4[3]);
+    uint8_t* q_row = (uint8_t*)a.q_out + (size_t)row * ((size_t)d * kCodeBits / 8);
+    if constexpr (MODE == kInt8) *(uint4*)(q_row + slot * kSlot) = make_uint4(q4[0], q4[1], q4[2], q4[3]);
+    else *(uint2*)(q_row + slot * (kSlot / 2)) = make_uint2(q4[0], q4[1]);
     if ((lane & (lanes - 1)) == 0)
       a.scale_out[(size_t)row * (d / a.group) + slot * kSlot / a.group] = sbits;
   }

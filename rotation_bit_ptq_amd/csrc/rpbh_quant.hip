@@ -85,6 +85,11 @@ hipError_t launch_rows(const RowJob& job, hipStream_t stream) {
       if (lt == 3) return launch_fast<kInt8, 3>(a, 0, stream);
       return launch_fast<kInt8, 4>(a, 0, stream);
     }
+    if (job.mode == RowMode::kInt4Pack) {
+      if (lt == 2) return launch_fast<kInt4, 2>(a, 0, stream);
+      if (lt == 3) return launch_fast<kInt4, 3>(a, 0, stream);
+      return launch_fast<kInt4, 4>(a, 0, stream);
+    }
     if (job.out_dtype == ORBIT_F16) {
       if (lt == 2) return launch_fast<kRotF16, 2>(a, 0, stream);
       if (lt == 3) return launch_fast<kRotF16, 3>(a, 0, stream);
@@ -110,6 +115,9 @@ hipError_t launch_rows(const RowJob& job, hipStream_t stream) {
     case RowMode::kInt8Pack:
       return bf16 ? launch_mode<uint16_t, kInt8>(a, 0, stream)
                   : launch_mode<float, kInt8>(a, 0, stream);
+    case RowMode::kInt4Pack:
+      return bf16 ? launch_mode<uint16_t, kInt4>(a, 0, stream)
+                  : launch_mode<float, kInt4>(a, 0, stream);
   }
   return hipErrorInvalidValue;
 }
