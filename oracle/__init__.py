@@ -50,7 +50,8 @@ from .numfmt import (bf16_bits_to_f64, f64_to_bf16_bits, f16_bits_to_f64,
 from .hadamard import sylvester, fwht
 from .rotation import (rpbh_matrix, rpbh_rotate, rpbh_inverse_rotate,
                        block_rht_rotate, full_rht_rotate, haar_matrix)
-from .codebook import lloyd_max_gaussian, codebook
+from .codebook import (lloyd_max_gaussian, codebook, lloyd_max_sphere, codebook_sphere,
+                       sphere_distortion)
 from .orbit import (quantize_codes, boundary_band, pack_indices, unpack_indices,
                     pack_weights, quant_act, qlinear_codes, qlinear_unquantized,
                     gelu_erf)
@@ -61,7 +62,8 @@ __all__ = [
     "bf16_bits_to_f64", "f64_to_bf16_bits", "f16_bits_to_f64", "f64_to_f16_bits",
     "f64_to_f32", "sylvester", "fwht", "rpbh_matrix", "rpbh_rotate",
     "rpbh_inverse_rotate", "block_rht_rotate", "full_rht_rotate", "haar_matrix",
-    "lloyd_max_gaussian", "codebook", "quantize_codes", "boundary_band",
+    "lloyd_max_gaussian", "codebook", "lloyd_max_sphere", "codebook_sphere",
+    "sphere_distortion", "quantize_codes", "boundary_band",
     "pack_indices", "unpack_indices", "pack_weights", "quant_act",
     "qlinear_codes", "qlinear_unquantized", "gelu_erf", "int8_pack",
     "int8_dequant", "int8_linear", "int4_pack", "int4_dequant", "int4_linear",
