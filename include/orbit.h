@@ -133,6 +133,18 @@ orbit_status orbit_fit_codebook(int32_t d, int32_t bits, int32_t max_iter, doubl
                                 orbit_codebook *out, double *centroids_f64,
                                 double *thresholds_f64, double *mse_f64);
 
+/* Lloyd-Max codebook on the exact marginal f_d (OrbitQuant page, Method):
+ * one coordinate T of a direction uniform on the unit sphere S^{d-1}, with
+ * density proportional to (1 - t^2)^((d-3)/2), in N(0,1) units u = sqrt(d) t
+ * (so |u| <= sqrt(d) and E[u^2] = 1).  As d grows it tends to the N(0,1)
+ * codebook of orbit_fit_codebook; for d = 3 it is the uniform quantizer of
+ * [-sqrt 3, sqrt 3].  Arguments, outputs and method as orbit_fit_codebook.
+ * Errors: ORBIT_E_ARG (bits not in {1,2,3,4,6,8}, out NULL, d < 3),
+ * ORBIT_E_UNSUPPORTED (no ordered fixed point reached). */
+orbit_status orbit_fit_codebook_sphere(int32_t d, int32_t bits, int32_t max_iter, double tol,
+                                       orbit_codebook *out, double *centroids_f64,
+                                       double *thresholds_f64, double *mse_f64);
+
 /* Offline weight packer (OrbitQuant page, Method, offline stage):
  * W' = W Pi^T row by row, r_n = ||w'_n|| rounded to bf16 (nearest even),
  * u = sqrt(d) w'_n / r_n (u = 0 for a zero row), idx = #{t_j < u}.

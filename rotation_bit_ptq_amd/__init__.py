@@ -63,6 +63,7 @@ def _load():
         "orbit_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "orbit_last_hip_error": ([], ctypes.c_int),
         "orbit_fit_codebook": ([I32, I32, I32, D, P, P, P, P], ctypes.c_int),
+        "orbit_fit_codebook_sphere": ([I32, I32, I32, D, P, P, P, P], ctypes.c_int),
         "orbit_rpbh_gather_len": ([I32, I32], I64),
         "orbit_rpbh_build_gather": ([P, P, P], ctypes.c_int),
         "orbit_pack_weights": ([P, P, P, ctypes.c_int, I64, I64, P, P, P], ctypes.c_int),
@@ -122,21 +123,29 @@ def packed_row_bytes(d: int, bits: int) -> int:
 
 
 class Codebook:
-    """A Lloyd-Max codebook in N(0,1) units (host memory)."""
+    """A Lloyd-Max codebook in N(0,1) units (host memory).
 
-    def __init__(self, d: int, bits: int, max_iter: int = 0, tol: float = 0.0):
+    marginal="gauss": fitted to N(0,1), the large-d form of the rotated
+    coordinate's marginal; "sphere": fitted to the exact marginal of one
+    coordinate of a uniform direction on S^{d-1} (d >= 3)."""
+
+    def __init__(self, d: int, bits: int, max_iter: int = 0, tol: float = 0.0,
+                 marginal: str = "gauss"):
+        fitters = {"gauss": "orbit_fit_codebook", "sphere": "orbit_fit_codebook_sphere"}
+        if marginal not in fitters:
+            raise ValueError(f"marginal must be one of {sorted(fitters)}")
         levels = 1 << bits
         self.struct = _Codebook()
         self.centroids_f64 = np.zeros(levels)
         self.thresholds_f64 = np.zeros(levels - 1)
         mse = ctypes.c_double(0.0)
-        _check(lib.orbit_fit_codebook(
+        _check(getattr(lib, fitters[marginal])(
             d, bits, max_iter, tol, ctypes.byref(self.struct),
             self.centroids_f64.ctypes.data_as(ctypes.c_void_p),
             self.thresholds_f64.ctypes.data_as(ctypes.c_void_p), ctypes.byref(mse)),
-            "orbit_fit_codebook")
+            fitters[marginal])
         self.mse = mse.value
-        self.bits, self.d, self.levels = bits, d, levels
+        self.bits, self.d, self.levels, self.marginal = bits, d, levels, marginal
 
     @property
     def centroids(self) -> np.ndarray:
@@ -147,8 +156,8 @@ class Codebook:
         return np.ctypeslib.as_array(self.struct.thresholds)[: self.levels - 1].copy()
 
 
-def fit_codebook(d: int, bits: int) -> Codebook:
-    return Codebook(d, bits)
+def fit_codebook(d: int, bits: int, marginal: str = "gauss") -> Codebook:
+    return Codebook(d, bits, marginal=marginal)
 
 
 class Rotation:

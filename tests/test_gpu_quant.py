@@ -18,11 +18,11 @@ pytestmark = pytest.mark.gpu
 EPS = synth.EPS
 
 
-def _run_act(rbp, X, perm, signs, h, bits, label):
+def _run_act(rbp, X, perm, signs, h, bits, label, marginal="gauss"):
     d = X.shape[1]
     rot = rbp.Rotation(perm, signs, h)
-    cb = rbp.Codebook(d, bits)
-    ref_cb = oracle.codebook(bits)
+    cb = rbp.Codebook(d, bits, marginal=marginal)
+    ref_cb = oracle.codebook(bits) if marginal == "gauss" else oracle.codebook_sphere(bits, d)
     idx, s, xr = rbp.quant_act(rot, cb, to_dev(X), EPS, debug_xrot=True)
     torch.cuda.synchronize()
     ref = oracle.quant_act(as_f64(X), perm, signs, h, ref_cb, bits, EPS)
@@ -56,7 +56,16 @@ def test_quant_act_other_widths(gpu_lib, bits):
     _run_act(gpu_lib, inp["X"], inp["perm"], inp["signs"], inp["h"], bits, f"a{bits}")
 
 
-def test_quant_act_long_rows_two_pass(gpu_lib):
+@pytest.mark.parametrize("cfg,bits", [(1, 4), (2, 4), (2, 3), (5, 6)])
+def test_quant_act_sphere_codebook(gpu_lib, cfg, bits):
+    # the codebook of the exact sphere marginal f_d: the kernels read only
+    # its float32 thresholds, so parity is the same as for N(0,1) tables
+    inp = synth.make(cfg, M=128, N=8)
+    _run_act(gpu_lib, inp["X"], inp["perm"], inp["signs"], inp["h"], bits,
+             f"sphere-cfg{cfg}-a{bits}", marginal="sphere")
+
+
+def test_quant_act_long_rows(gpu_lib):
     # d = 12288 (the MLP down projection input, 48 blocks of 256): rows longer
     # than 4096 take the two-pass path
     inp = synth.make(4, M=8)

@@ -42,6 +42,40 @@ def test_fitter_agrees_with_oracle(bits):
     assert cb.thresholds[2 ** (bits - 1) - 1] == 0.0
 
 
+@pytest.mark.parametrize("d", [3, 4, 16, 64, 3072, 12288])
+@pytest.mark.parametrize("bits", [1, 2, 4, 6, 8])
+def test_sphere_fitter_agrees_with_oracle(d, bits):
+    # the library evaluates the incomplete beta with its own continued
+    # fraction and solves by Newton; the oracle calls scipy's betaincc and
+    # MINPACK: both must land on the unique (f_d is log-concave for d >= 3)
+    # fixed point.  Evaluated with 40-digit functions (mpmath), both fits
+    # leave a residual of ~4e-12 (the tails are good to ~3e-15 relative), and
+    # the fixed point's condition number grows like L^2 for L levels (its
+    # slowest Lloyd modes), so the two solutions may differ by ~1e-12 L^2;
+    # the float32 tables the kernels read may differ by one ulp at most.
+    L = 2 ** bits
+    cb = _lib().Codebook(d, bits, marginal="sphere")
+    ref = oracle.lloyd_max_sphere(L, d)
+    np.testing.assert_allclose(cb.centroids_f64, ref["centroids"], rtol=0, atol=1e-12 * L * L)
+    np.testing.assert_allclose(cb.thresholds_f64, ref["thresholds"], rtol=0, atol=1e-12 * L * L)
+    assert abs(cb.mse - ref["distortion"]) < 1e-11
+    for got, want in ((cb.centroids, ref["centroids"]), (cb.thresholds, ref["thresholds"])):
+        ulps = np.abs(got.view(np.int32).astype(np.int64)
+                      - want.astype(np.float32).view(np.int32).astype(np.int64))
+        assert ulps.max() <= 1
+    assert cb.thresholds[2 ** (bits - 1) - 1] == 0.0
+    assert cb.marginal == "sphere" and cb.d == d
+
+
+def test_sphere_fit_errors():
+    cb = _lib()._Codebook()
+    assert _call("orbit_fit_codebook_sphere", 2, 4, 0, 0.0, ctypes.byref(cb), None, None, None) == 1
+    assert _call("orbit_fit_codebook_sphere", 64, 5, 0, 0.0, ctypes.byref(cb), None, None, None) == 1
+    assert _call("orbit_fit_codebook_sphere", 64, 4, 0, 0.0, None, None, None, None) == 1
+    with pytest.raises(ValueError):
+        _lib().Codebook(64, 4, marginal="laplace")
+
+
 def _call(name, *args):
     fn = getattr(_lib().lib, name)
     return fn(*args)
