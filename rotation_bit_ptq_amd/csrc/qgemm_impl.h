@@ -220,6 +220,8 @@ struct F16Op {  // fp16 rows (rotated activations of the int8 GEMM)
 
 struct I8Op {  // int8 weight rows with an fp16 scale for the chunk's group
   static constexpr int kChunkK = 32;
+  static constexpr int kCodeBits = 8;
+  typedef u32x4 Raw;  // 16 codes: two sub-steps of 8
   static constexpr int kBytes = 16;  // 16 codes per lane per chunk
   u32x4 v;
   uint32_t scale2;  // the group's fp16 scale in both halves
@@ -253,6 +255,8 @@ struct I4Op {  // int4 weight rows (two's-complement nibbles, low nibble
                // first) with an fp16 scale for the chunk's group
   static constexpr int kChunkK = 32;
   static constexpr int kBytes = 8;  // 16 codes per lane per chunk
+  static constexpr int kCodeBits = 4;
+  typedef uint2 Raw;  // 16 codes: two sub-steps of 8
   uint2 v;
   uint32_t scale2;  // the group's fp16 scale in both halves
   __device__ __forceinline__ void load(const uint8_t* p) { v = *(const uint2*)p; }
@@ -366,7 +370,18 @@ __device__ __forceinline__ void issue_schedule(std::integer_sequence<int, K...>)
   (issue_slot<NMF, NDS, NVA, NVM, K>(), ...);
 }
 
-// KIND 0: codebook x codebook; KIND 1: fp16 x int8 or int4 with group scales.
+// s_waitcnt immediate that waits until at most N vector memory loads are in
+// flight (vmcnt, bits 3:0 and 15:14) and leaves the LDS/scalar and export
+// counters unconstrained.
+template <int N>
+constexpr int vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+  return (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
+}
+
+// KIND 0: codebook x codebook; KIND 1: fp16 x int8 or int4 with group scales,
+// operands straight from memory; KIND 2: the same product with both operands
+// staged through a three-chunk LDS ring (256 x 256 tiles).
 // WM token blocks and WN weight blocks of 32 per wave.
 template <int KIND, class OpA, class OpB, int WM, int WN>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
@@ -525,7 +540,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
       chunk(1, c + 1);
     }
     if (c < nchunks) chunk(0, c);
-  } else {
+  } else if constexpr (KIND == 1) {
     // Raw codes of chunk c + 1 load into the other of two buffers while chunk
     // c is decoded and multiplied.  Decoded token operands are single-
     // buffered: block i is re-decoded for the next sub-step right after its
@@ -612,6 +627,182 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
     } else {                // one chunk left
       chunk_last(ra0, rb0);
     }
+  } else {
+    // KIND 2.  Chunks of 64 k; chunk c lives in LDS stage c % 3 while the
+    // loads of chunks c + 1 and c + 2 are in flight.  Loads go global -> LDS
+    // directly (16 bytes per lane, written in lane order), so data in flight
+    // holds no registers.  Stage layout, in 1 KB blocks (one load instruction
+    // each):
+    //   tokens (fp16): block b = rows 8b..8b+7, 128 bytes (64 k) each; lane i
+    //     carries row 8b + i/8, 16-byte piece (i % 8) ^ (i / 8);
+    //   weights, int8: block b = rows 16b..16b+15, 64 bytes each; lane i
+    //     carries row 16b + i/4, 16-byte unit (i % 4) ^ ((i / 8) % 4);
+    //   weights, int4: block b = rows 32b..32b+31, 32 bytes each; lane i
+    //     carries row 32b + i/2, 16-byte unit (i % 2) ^ ((i / 8) % 2);
+    //   group scales: 256 dwords, tile row t at dword t, the aligned dword
+    //     that holds the fp16 scale of (row, chunk's group).
+    // The XOR swizzles make every group of 8 lanes of an operand read (same
+    // piece, 8 consecutive rows) hit 8 different 16-byte bank groups, while
+    // each load instruction still covers whole rows of the chunk.
+    // Per lane and sub-step s (v = s / 2) the MFMA k order is
+    //   k = 32 v + 16 half + 8 (s % 2) + 0..7
+    // for both operands: token piece 4 v + 2 half + s % 2; int8 unit 2 v +
+    // half (16 bytes, sub-steps 2v and 2v+1 at once); int4 unit v, bytes
+    // 8 half .. 8 half + 7.
+    // The loads are issued with inline assembly and waited for explicitly
+    // (vmcnt, then a bare s_barrier): they have no register results, and the
+    // compiler, which cannot tell the stages apart, would otherwise wait for
+    // every load in flight before each LDS read.
+    static_assert(WM == 4 && WN == 4, "the staged loop is laid out for 256 x 256 tiles");
+    constexpr int kCK = 64;
+    constexpr bool kI4 = OpB::kCodeBits == 4;
+    constexpr int kBRow = kCK * OpB::kCodeBits / 8;   // weight bytes per row per chunk
+    constexpr int kABytes = TM * kCK * 2;              // 32 KB
+    constexpr int kBBytes = TN * kBRow;                // 16 or 8 KB
+    constexpr int kSBytes = TN * 4;                    // scale dwords
+    constexpr int kStage = kABytes + kBBytes + kSBytes;
+    constexpr int kALoads = kABytes / 1024 / 4;        // per thread per chunk
+    constexpr int kBLoads = kBBytes / 1024 / 4;
+    constexpr int kLoads = kALoads + kBLoads + 1;
+    static_assert(kStage % 16 == 0, "stages stay 16-byte aligned");
+    const int nch = (int)(g.K / kCK);                  // >= 2 (K % 128 == 0)
+    const int last = nch - 1;
+    const uint32_t wv = __builtin_amdgcn_readfirstlane((uint32_t)wave);
+
+    // global sources of this thread's loads (rows past the end are clamped:
+    // valid memory, results dropped)
+    uint32_t ga[kALoads], gb[kBLoads];
+#pragma unroll
+    for (int q = 0; q < kALoads; ++q) {
+      const int blk = q * 4 + wave, r8 = lane >> 3;
+      long long m = (long long)tm * TM + 8 * blk + r8;
+      m = m < g.M ? m : g.M - 1;
+      ga[q] = (uint32_t)(m * g.lda) + (uint32_t)((((int)lane & 7) ^ r8) * 16);
+    }
+#pragma unroll
+    for (int q = 0; q < kBLoads; ++q) {
+      const int blk = q * 4 + wave;
+      int r, u;
+      if constexpr (kI4) {
+        r = 32 * blk + (lane >> 1);
+        u = ((int)lane & 1) ^ ((lane >> 3) & 1);
+      } else {
+        r = 16 * blk + (lane >> 2);
+        u = ((int)lane & 3) ^ ((lane >> 3) & 3);
+      }
+      long long n = (long long)tn * TN + r;
+      n = n < g.N ? n : g.N - 1;
+      gb[q] = (uint32_t)(n * g.ldb) + (uint32_t)(u * 16);
+    }
+    // scale element of (tile row t, group 0); the dword holding element e
+    // starts at byte 2 (e & ~1), and element e is its half e & 1
+    uint32_t gs;
+    {
+      long long n = (long long)tn * TN + t;
+      n = n < g.N ? n : g.N - 1;
+      gs = (uint32_t)n * (uint32_t)g.groups_per_row;
+    }
+    // loads chunk c (clamped to the last chunk) into the stage of chunk cs
+    auto issue = [&](int cs, int c) {
+      c = c < last ? c : last;
+      const uint32_t st = (uint32_t)(cs % 3) * kStage;
+#pragma unroll
+      for (int q = 0; q < kALoads; ++q)
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                     :: "s"(st + (q * 4 + wv) * 1024u), "v"(ga[q] + (uint32_t)c * (kCK * 2)), "s"(g.a)
+                     : "memory", "m0");
+#pragma unroll
+      for (int q = 0; q < kBLoads; ++q)
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                     :: "s"(st + kABytes + (q * 4 + wv) * 1024u), "v"(gb[q] + (uint32_t)c * kBRow), "s"(g.b)
+                     : "memory", "m0");
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+                   :: "s"(st + kABytes + kBBytes + wv * 256u), "v"(((gs + (uint32_t)(c >> 1)) & ~1u) * 2u),
+                      "s"(g.scale_f16)
+                   : "memory", "m0");
+    };
+    // this lane's LDS read offsets inside a stage
+    const uint32_t xa = r32 & 7;
+    const uint32_t a_base = (uint32_t)(wm * 16 + (r32 >> 3)) * 1024u + xa * 128u;
+    uint32_t a_off[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      a_off[s] = a_base + (((uint32_t)(4 * (s >> 1) + 2 * half + (s & 1)) ^ xa) << 4);
+    uint32_t b_off[2];
+    constexpr uint32_t kBBlock = kI4 ? 1024u : 2048u;  // LDS bytes per 32 weight rows
+    if constexpr (kI4) {
+      const uint32_t x4 = (r32 >> 2) & 1;
+      const uint32_t b_base = (uint32_t)kABytes + (uint32_t)(wn * 4) * 1024u + r32 * 32u + (uint32_t)half * 8u;
+#pragma unroll
+      for (int v = 0; v < 2; ++v) b_off[v] = b_base + (((uint32_t)v ^ x4) << 4);
+    } else {
+      const uint32_t r16 = r32 & 15, x8 = (r16 >> 1) & 3;
+      const uint32_t b_base = (uint32_t)kABytes + (uint32_t)(wn * 8 + (r32 >> 4)) * 1024u + r16 * 64u;
+#pragma unroll
+      for (int v = 0; v < 2; ++v) b_off[v] = b_base + (((uint32_t)(2 * v + half) ^ x8) << 4);
+    }
+    const uint32_t s_off = (uint32_t)(kABytes + kBBytes) + (uint32_t)(wn * 128 + r32) * 4u;
+    uint32_t s_par[WN];  // parity of the lane's scale element at group 0
+#pragma unroll
+    for (int j = 0; j < WN; ++j) s_par[j] = (nrow[j] * (uint32_t)g.groups_per_row) & 1u;
+
+    // Every iteration issues the same kLoads loads into stage (c + 2) % 3
+    // (chunk c + 2, or a re-read of the last chunk that nobody reads again),
+    // so waiting until at most kLoads are in flight completes chunk c + 1.
+    // The wait also drains this wave's LDS reads (lgkmcnt 0), and the empty
+    // asm statements keep the compiler from moving memory accesses across
+    // the barrier.
+    auto sync = [&]() {
+      __builtin_amdgcn_s_waitcnt(vm_wait<kLoads>() & ~(15 << 8));
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+    issue(0, 0);
+    issue(1, 1);
+    sync();
+    for (int c = 0; c < nch; ++c) {
+      // chunk c is complete in stage c % 3 for every thread, and every wave
+      // is done reading stage (c + 2) % 3 (chunk c - 1)
+      issue(c + 2, c + 2);
+      const char* const st = smem + (c % 3) * kStage;
+      uint32_t sc[WN];
+#pragma unroll
+      for (int j = 0; j < WN; ++j) {
+        const uint32_t dw = *(const uint32_t*)(st + s_off + j * 128);
+        const uint32_t h16 = (dw >> (16 * ((s_par[j] + (uint32_t)(c >> 1)) & 1u))) & 0xffffu;
+        sc[j] = h16 | (h16 << 16);
+      }
+      typename OpB::Raw braw[WN];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        if ((s & 1) == 0) {
+#pragma unroll
+          for (int j = 0; j < WN; ++j)
+            braw[j] = *(const typename OpB::Raw*)(st + b_off[s >> 1] + j * kBBlock);
+        }
+        half8 av[WM], bv[WN];
+#pragma unroll
+        for (int i = 0; i < WM; ++i) av[i] = *(const half8*)(st + a_off[s] + i * 4096);
+#pragma unroll
+        for (int j = 0; j < WN; ++j) {
+          OpB op;
+          op.v = braw[j];
+          op.scale2 = sc[j];
+          bv[j] = op.decode(s & 1, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < WN; ++j)
+#pragma unroll
+          for (int i = 0; i < WM; ++i)
+            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bv[j], av[i], acc[j][i], 0, 0, 0);
+      }
+      // chunk c + 1 (issued one iteration ago) complete; the LDS reads of
+      // this chunk are done before any wave passes the barrier
+      sync();
+    }
+    // the trailing re-reads must land before the epilogue reuses the ring
+    __builtin_amdgcn_s_waitcnt(vm_wait<0>());
   }
 
   // epilogue: block (j, i) of lane l holds weight rows

@@ -126,3 +126,26 @@ def test_int4_rejects_bad_shapes(gpu_lib):
         rbp.int4_linear(xr, q, sc, 64)                # group must be 128
     with pytest.raises(ValueError):
         rbp.int4_linear(xr, q[:, :64].contiguous(), sc, 128)
+
+
+# Products with at least 128 tiles of 256 x 256 take the LDS-staged kernel;
+# (4096, 2049, 384) has an odd number of scale entries and takes the
+# register-fed kernel instead.
+STAGED = [(4096, 2048, 512), (4000, 2100, 256), (4096, 2048, 128), (4096, 2049, 384)]
+
+
+@pytest.mark.parametrize("M,N,K", STAGED)
+def test_int4_linear_staged_tiles(gpu_lib, M, N, K):
+    rbp = gpu_lib
+    inp = synth.make(3, M=M, N=N, K=K, h=128)
+    rot = rbp.Rotation(inp["perm"], inp["signs"], 128)
+    q, sc = rbp.int4_pack_weights(rot, to_dev(inp["W"]), 128)
+    xr = rbp.rotate(rot, to_dev(inp["X"]), torch.float16)
+    bias = torch.from_numpy(np.random.default_rng(3).standard_normal(N).astype(np.float32)).cuda()
+    qi = int4.unpack_nibbles(q.cpu().numpy(), K)
+    x16 = oracle.f16_bits_to_f64(bits_of(xr))
+    y = int4.int4_linear_rotated(x16, qi, bits_of(sc)) + bias.cpu().numpy()
+    out32 = rbp.int4_linear(xr, q, sc, 128, bias=bias, out_dtype=torch.float32)
+    assert rel_fro(out_f64(out32), y) < SAME_X_TOL
+    out16 = rbp.int4_linear(xr, q, sc, 128, bias=bias)
+    assert rel_fro(out_f64(out16), y) < OUT_TOL

@@ -88,3 +88,28 @@ def test_int8_linear_ragged(gpu_lib, M, N):
     y, _ = oracle.int8_linear(as_f64(inp["X"]), q.cpu().numpy(), bits_of(sc), inp["perm"],
                               inp["signs"], inp["h"], 128)
     assert rel_fro(out_f64(out), y + bias.cpu().numpy()) < OUT_TOL
+
+
+# Products with at least 128 tiles of 256 x 256 take the LDS-staged kernel;
+# (4096, 2049, 384) has an odd number of scale entries and takes the
+# register-fed kernel instead.  On the GPU's own fp16 x' the result differs
+# from the exact product only by the fp16 rounding of each decoded weight
+# (relative <= 2^-11) and fp32 accumulation.
+STAGED = [(4096, 2048, 512), (4000, 2100, 256), (4096, 2048, 128), (4096, 2049, 384)]
+
+
+@pytest.mark.parametrize("M,N,K", STAGED)
+def test_int8_linear_staged_tiles(gpu_lib, M, N, K):
+    from oracle.int8 import int8_linear_rotated
+    rbp = gpu_lib
+    inp = synth.make(3, M=M, N=N, K=K, h=128)
+    rot = rbp.Rotation(inp["perm"], inp["signs"], 128)
+    q, sc = rbp.int8_pack_weights(rot, to_dev(inp["W"]), 128)
+    xr = rbp.rotate(rot, to_dev(inp["X"]), torch.float16)
+    bias = torch.from_numpy(np.random.default_rng(3).standard_normal(N).astype(np.float32)).cuda()
+    x16 = oracle.f16_bits_to_f64(bits_of(xr))
+    y = int8_linear_rotated(x16, q.cpu().numpy(), bits_of(sc), 128) + bias.cpu().numpy()
+    out32 = rbp.int8_linear(xr, q, sc, 128, bias=bias, out_dtype=torch.float32)
+    assert rel_fro(out_f64(out32), y) < 2.0 ** -11
+    out16 = rbp.int8_linear(xr, q, sc, 128, bias=bias)
+    assert rel_fro(out_f64(out16), y) < OUT_TOL
