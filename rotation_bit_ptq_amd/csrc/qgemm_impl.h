@@ -370,6 +370,15 @@ __device__ __forceinline__ void issue_schedule(std::integer_sequence<int, K...>)
   (issue_slot<NMF, NDS, NVA, NVM, K>(), ...);
 }
 
+// Wave grid of a workgroup (4 waves): 2 x 2 for the register-fed kernels,
+// 1 x 4 for the staged weight-only kernel (each wave spans all 256 tokens of
+// the tile and 64 weight rows, so every decoded weight fragment feeds eight
+// MFMAs and no two waves decode the same weights).
+template <int KIND>
+struct WavesM {
+  static constexpr int value = KIND == 2 ? 1 : 2;
+};
+
 // s_waitcnt immediate that waits until at most N vector memory loads are in
 // flight (vmcnt, bits 3:0 and 15:14) and leaves the LDS/scalar and export
 // counters unconstrained.
@@ -389,10 +398,11 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
   static_assert(OpA::kChunkK == OpB::kChunkK, "operands must share the chunk");
   constexpr int KC = OpA::kChunkK;
   constexpr int STEPS = KC / 16;
-  constexpr int TM = 64 * WM, TN = 64 * WN;
+  constexpr int kWM = WavesM<KIND>::value, kWN = 4 / kWM;  // wave grid
+  constexpr int TM = 32 * WM * kWM, TN = 32 * WN * kWN;
   const uint32_t lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % kWM, wn = wave / kWM;
 
   int tm, tn;
   tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
@@ -427,8 +437,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
   const uint32_t lb_a = OpA::lane_base((uint32_t)g.table_a_offset, lane);
   const uint32_t lb_b = OpB::lane_base((uint32_t)g.table_b_offset, lane);
 
-  const long long m_base = (long long)tm * TM + wm * (TM / 2);
-  const long long n_base = (long long)tn * TN + wn * (TN / 2);
+  const long long m_base = (long long)tm * TM + wm * (32 * WM);
+  const long long n_base = (long long)tn * TN + wn * (32 * WN);
   const int r32 = lane & 31, half = lane >> 5;
 
   // row offsets (rows past the end are clamped; their results are dropped);
@@ -631,29 +641,31 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
     // KIND 2.  Chunks of 64 k; chunk c lives in LDS stage c % 3 while the
     // loads of chunks c + 1 and c + 2 are in flight.  Loads go global -> LDS
     // directly (16 bytes per lane, written in lane order), so data in flight
-    // holds no registers.  Stage layout, in 1 KB blocks (one load instruction
-    // each):
-    //   tokens (fp16): block b = rows 8b..8b+7, 128 bytes (64 k) each; lane i
-    //     carries row 8b + i/8, 16-byte piece (i % 8) ^ (i / 8);
-    //   weights, int8: block b = rows 16b..16b+15, 64 bytes each; lane i
-    //     carries row 16b + i/4, 16-byte unit (i % 4) ^ ((i / 8) % 4);
-    //   weights, int4: block b = rows 32b..32b+31, 32 bytes each; lane i
-    //     carries row 32b + i/2, 16-byte unit (i % 2) ^ ((i / 8) % 2);
+    // holds no registers.  Per lane and sub-step s the MFMA k order is
+    //   k = 32 half + 8 s + 0..7
+    // for both operands, so a lane's k of one chunk are 32 consecutive
+    // values.  Stage layout, in 1 KB blocks (one load instruction each), with
+    // row r counted inside its block:
+    //   tokens (fp16): rows 8b..8b+7 of 128 bytes (64 k); 16-byte piece p of
+    //     row r sits at r * 128 + (p ^ ((r / 2) % 8)) * 16 (a lane reads
+    //     piece 4 half + s);
+    //   weights, int8: rows 16b..16b+15 of 64 bytes; 16-byte unit u at
+    //     r * 64 + (u ^ ((r / 4) % 4)) * 16 (a lane reads unit 2 half + s/2,
+    //     two sub-steps at once);
+    //   weights, int4: rows 32b..32b+31 of 32 bytes; 16-byte unit u at
+    //     r * 32 + (u ^ ((r / 8) % 2)) * 16 (a lane reads unit half once per
+    //     chunk, all four sub-steps);
     //   group scales: 256 dwords, tile row t at dword t, the aligned dword
     //     that holds the fp16 scale of (row, chunk's group).
-    // The XOR swizzles make every group of 8 lanes of an operand read (same
-    // piece, 8 consecutive rows) hit 8 different 16-byte bank groups, while
-    // each load instruction still covers whole rows of the chunk.
-    // Per lane and sub-step s (v = s / 2) the MFMA k order is
-    //   k = 32 v + 16 half + 8 (s % 2) + 0..7
-    // for both operands: token piece 4 v + 2 half + s % 2; int8 unit 2 v +
-    // half (16 bytes, sub-steps 2v and 2v+1 at once); int4 unit v, bytes
-    // 8 half .. 8 half + 7.
+    // LDS serves a 16-byte read for 16 lanes (16 consecutive rows) at a
+    // time across 256 bytes; the XOR swizzles put those 16 rows in 16
+    // different 16-byte bank groups, while each load instruction still
+    // covers whole rows of the chunk.
     // The loads are issued with inline assembly and waited for explicitly
     // (vmcnt, then a bare s_barrier): they have no register results, and the
     // compiler, which cannot tell the stages apart, would otherwise wait for
     // every load in flight before each LDS read.
-    static_assert(WM == 4 && WN == 4, "the staged loop is laid out for 256 x 256 tiles");
+    static_assert(WM == 8 && WN == 2 && kWM == 1, "the staged loop is laid out for 256 x 256 tiles, 1 x 4 waves");
     constexpr int kCK = 64;
     constexpr bool kI4 = OpB::kCodeBits == 4;
     constexpr int kBRow = kCK * OpB::kCodeBits / 8;   // weight bytes per row per chunk
@@ -677,7 +689,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
       const int blk = q * 4 + wave, r8 = lane >> 3;
       long long m = (long long)tm * TM + 8 * blk + r8;
       m = m < g.M ? m : g.M - 1;
-      ga[q] = (uint32_t)(m * g.lda) + (uint32_t)((((int)lane & 7) ^ r8) * 16);
+      const int f = ((8 * blk + r8) >> 1) & 7;
+      ga[q] = (uint32_t)(m * g.lda) + (uint32_t)((((int)lane & 7) ^ f) * 16);
     }
 #pragma unroll
     for (int q = 0; q < kBLoads; ++q) {
@@ -685,10 +698,10 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
       int r, u;
       if constexpr (kI4) {
         r = 32 * blk + (lane >> 1);
-        u = ((int)lane & 1) ^ ((lane >> 3) & 1);
+        u = ((int)lane & 1) ^ ((lane >> 4) & 1);
       } else {
         r = 16 * blk + (lane >> 2);
-        u = ((int)lane & 3) ^ ((lane >> 3) & 3);
+        u = ((int)lane & 3) ^ ((lane >> 4) & 3);
       }
       long long n = (long long)tn * TN + r;
       n = n < g.N ? n : g.N - 1;
@@ -722,36 +735,73 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
                    : "memory", "m0");
     };
     // this lane's LDS read offsets inside a stage
-    const uint32_t xa = r32 & 7;
-    const uint32_t a_base = (uint32_t)(wm * 16 + (r32 >> 3)) * 1024u + xa * 128u;
+    const uint32_t xa = (r32 >> 1) & 7;
+    const uint32_t a_base = (uint32_t)(wm * 4 * WM + (r32 >> 3)) * 1024u + (r32 & 7) * 128u;
     uint32_t a_off[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      a_off[s] = a_base + (((uint32_t)(4 * (s >> 1) + 2 * half + (s & 1)) ^ xa) << 4);
+    for (int s = 0; s < 4; ++s) a_off[s] = a_base + (((uint32_t)(4 * half + s) ^ xa) << 4);
     uint32_t b_off[2];
     constexpr uint32_t kBBlock = kI4 ? 1024u : 2048u;  // LDS bytes per 32 weight rows
     if constexpr (kI4) {
-      const uint32_t x4 = (r32 >> 2) & 1;
-      const uint32_t b_base = (uint32_t)kABytes + (uint32_t)(wn * 4) * 1024u + r32 * 32u + (uint32_t)half * 8u;
-#pragma unroll
-      for (int v = 0; v < 2; ++v) b_off[v] = b_base + (((uint32_t)v ^ x4) << 4);
+      const uint32_t x4 = (r32 >> 3) & 1;
+      b_off[0] = (uint32_t)kABytes + (uint32_t)(wn * WN) * 1024u + r32 * 32u + (((uint32_t)half ^ x4) << 4);
+      b_off[1] = b_off[0];
     } else {
-      const uint32_t r16 = r32 & 15, x8 = (r16 >> 1) & 3;
-      const uint32_t b_base = (uint32_t)kABytes + (uint32_t)(wn * 8 + (r32 >> 4)) * 1024u + r16 * 64u;
+      const uint32_t r16 = r32 & 15, x8 = (r16 >> 2) & 3;
+      const uint32_t b_base = (uint32_t)kABytes + (uint32_t)(wn * 2 * WN + (r32 >> 4)) * 1024u + r16 * 64u;
 #pragma unroll
-      for (int v = 0; v < 2; ++v) b_off[v] = b_base + (((uint32_t)(2 * v + half) ^ x8) << 4);
+      for (int v = 0; v < 2; ++v) b_off[v] = b_base + (((uint32_t)(2 * half + v) ^ x8) << 4);
     }
-    const uint32_t s_off = (uint32_t)(kABytes + kBBytes) + (uint32_t)(wn * 128 + r32) * 4u;
+    const uint32_t s_off = (uint32_t)(kABytes + kBBytes) + (uint32_t)(wn * 32 * WN + r32) * 4u;
     uint32_t s_par[WN];  // parity of the lane's scale element at group 0
 #pragma unroll
     for (int j = 0; j < WN; ++j) s_par[j] = (nrow[j] * (uint32_t)g.groups_per_row) & 1u;
 
-    // Every iteration issues the same kLoads loads into stage (c + 2) % 3
-    // (chunk c + 2, or a re-read of the last chunk that nobody reads again),
-    // so waiting until at most kLoads are in flight completes chunk c + 1.
-    // The wait also drains this wave's LDS reads (lgkmcnt 0), and the empty
-    // asm statements keep the compiler from moving memory accesses across
-    // the barrier.
+    uint32_t sc[WN];
+    u32x4 braw[WN];  // int8: two sub-steps; int4: four
+    half8 a0[WM], a1[WM];
+    // sub-step s of the chunk in stage st on token operands a, whose next
+    // sub-step's token operands are read into an meanwhile; the weight
+    // operand of block j + 1 is decoded while block j's MFMAs run
+    auto substep = [&](auto s_, const char* st, const half8 (&a)[WM], half8 (&an)[WM]) {
+      constexpr int s = decltype(s_)::value;
+      if (kI4 ? s == 0 : (s & 1) == 0) {
+#pragma unroll
+        for (int j = 0; j < WN; ++j) braw[j] = *(const u32x4*)(st + b_off[s >> 1] + j * kBBlock);
+      }
+      if (s < 3) {
+#pragma unroll
+        for (int i = 0; i < WM; ++i) an[i] = *(const half8*)(st + a_off[s + 1] + i * 4096);
+      }
+#pragma unroll
+      for (int j = 0; j < WN; ++j) {
+        OpB op;
+        if constexpr (kI4) op.v = make_uint2(braw[j][s], 0u);
+        else op.v = braw[j];
+        op.scale2 = sc[j];
+        const half8 bv = op.decode(kI4 ? 0 : (s & 1), 0);
+#pragma unroll
+        for (int i = 0; i < WM; ++i)
+          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bv, a[i], acc[j][i], 0, 0, 0);
+      }
+      // reads first, then the first decode, then one MFMA per one or two
+      // decode instructions
+      __builtin_amdgcn_sched_group_barrier(0x100, (kI4 ? s == 0 : (s & 1) == 0) ? WN + WM : WM, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 14, 0);
+#pragma unroll
+      for (int q = 0; q < WM * WN; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Every chunk issues the same kLoads loads into stage (c + 2) % 3 (chunk
+    // c + 2, or a re-read of the last chunk that nobody reads again), so
+    // waiting until at most kLoads are in flight completes chunk c + 1.  The
+    // wait also drains this wave's LDS reads (lgkmcnt 0), and the empty asm
+    // statements keep the compiler from moving memory accesses across the
+    // barrier.
     auto sync = [&]() {
       __builtin_amdgcn_s_waitcnt(vm_wait<kLoads>() & ~(15 << 8));
       asm volatile("" ::: "memory");
@@ -766,40 +816,19 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
       // is done reading stage (c + 2) % 3 (chunk c - 1)
       issue(c + 2, c + 2);
       const char* const st = smem + (c % 3) * kStage;
-      uint32_t sc[WN];
 #pragma unroll
       for (int j = 0; j < WN; ++j) {
         const uint32_t dw = *(const uint32_t*)(st + s_off + j * 128);
         const uint32_t h16 = (dw >> (16 * ((s_par[j] + (uint32_t)(c >> 1)) & 1u))) & 0xffffu;
         sc[j] = h16 | (h16 << 16);
       }
-      typename OpB::Raw braw[WN];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        if ((s & 1) == 0) {
-#pragma unroll
-          for (int j = 0; j < WN; ++j)
-            braw[j] = *(const typename OpB::Raw*)(st + b_off[s >> 1] + j * kBBlock);
-        }
-        half8 av[WM], bv[WN];
-#pragma unroll
-        for (int i = 0; i < WM; ++i) av[i] = *(const half8*)(st + a_off[s] + i * 4096);
-#pragma unroll
-        for (int j = 0; j < WN; ++j) {
-          OpB op;
-          op.v = braw[j];
-          op.scale2 = sc[j];
-          bv[j] = op.decode(s & 1, 0);
-        }
-#pragma unroll
-        for (int j = 0; j < WN; ++j)
-#pragma unroll
-          for (int i = 0; i < WM; ++i)
-            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bv[j], av[i], acc[j][i], 0, 0, 0);
-      }
-      // chunk c + 1 (issued one iteration ago) complete; the LDS reads of
-      // this chunk are done before any wave passes the barrier
-      sync();
+      for (int i = 0; i < WM; ++i) a0[i] = *(const half8*)(st + a_off[0] + i * 4096);
+      substep(std::integral_constant<int, 0>{}, st, a0, a1);
+      substep(std::integral_constant<int, 1>{}, st, a1, a0);
+      substep(std::integral_constant<int, 2>{}, st, a0, a1);
+      substep(std::integral_constant<int, 3>{}, st, a1, a0);
+      sync();  // chunk c + 1 complete; this chunk's LDS reads are done
     }
     // the trailing re-reads must land before the epilogue reuses the ring
     __builtin_amdgcn_s_waitcnt(vm_wait<0>());
@@ -810,9 +839,9 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
   // The factors come from LDS.  A wave whose outputs lie inside the matrix,
   // with row length and output pointer aligned for 8/16-byte stores, takes
   // the vector path with no per-element checks.
-  const float* const ws = fs + wm * (TM / 2) + r32;
-  const float* const wr = fr + wn * (TN / 2) + 4 * half;
-  const float* const wb = fb + wn * (TN / 2) + 4 * half;
+  const float* const ws = fs + wm * (32 * WM) + r32;
+  const float* const wr = fr + wn * (32 * WN) + 4 * half;
+  const float* const wb = fb + wn * (32 * WN) + 4 * half;
   float sm[WM];
 #pragma unroll
   for (int i = 0; i < WM; ++i) sm[i] = ws[32 * i];
@@ -820,8 +849,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
   auto finish = [&](auto actc) {
     constexpr int ACT = decltype(actc)::value;
     const bool f32_out = g.out_dtype != ORBIT_BF16;
-    const bool fast = (g.N & 3) == 0 && ((uintptr_t)g.out & 15) == 0 && m_base + TM / 2 <= g.M &&
-                      n_base + TN / 2 <= g.N;
+    const bool fast = (g.N & 3) == 0 && ((uintptr_t)g.out & 15) == 0 && m_base + 32 * WM <= g.M &&
+                      n_base + 32 * WN <= g.N;
     auto epi = [&](auto f32c) {
       constexpr bool F32 = decltype(f32c)::value;
 #pragma unroll
@@ -860,7 +889,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
     if (staged) {
       constexpr int kRow = TN * 2 + 16;  // padded LDS row: 2-way bank conflicts at most
       __syncthreads();                   // every wave is done with the tables
-      const int lm = wm * (TM / 2) + r32, ln = wn * (TN / 2) + 4 * half;
+      const int lm = wm * (32 * WM) + r32, ln = wn * (32 * WN) + 4 * half;
 #pragma unroll
       for (int j = 0; j < WN; ++j) {
 #pragma unroll
@@ -923,7 +952,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
 
 template <int KIND, class OpA, class OpB, int WM, int WN>
 hipError_t launch_tile(GemmArgs& g, int lds, hipStream_t stream) {
-  constexpr int TM = 64 * WM, TN = 64 * WN;
+  constexpr int kWM = WavesM<KIND>::value, kWN = 4 / kWM;
+  constexpr int TM = 32 * WM * kWM, TN = 32 * WN * kWN;
   g.tiles_m = (int)((g.M + TM - 1) / TM);
   g.tiles_n = (int)((g.N + TN - 1) / TN);
   const long long tiles = (long long)g.tiles_m * g.tiles_n;

@@ -18,7 +18,7 @@ hipError_t launch_weight_only(GemmArgs& g, hipStream_t stream) {
   const bool scales_ok = ((uintptr_t)g.scale_f16 & 3) == 0 && (g.N * g.groups_per_row) % 2 == 0;
   if (tiles >= 128 && scales_ok) {
     constexpr int kStage = 256 * 64 * 2 + 256 * 64 * OpB::kCodeBits / 8 + 256 * 4;
-    return launch_tile<2, F16Op, OpB, 4, 4>(g, 3 * kStage, stream);
+    return launch_tile<2, F16Op, OpB, 8, 2>(g, 3 * kStage, stream);
   }
   return launch_shape<1, F16Op, OpB>(g, 0, stream);
 }
