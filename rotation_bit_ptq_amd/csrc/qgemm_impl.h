@@ -769,7 +769,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < WN; ++j) braw[j] = *(const u32x4*)(st + b_off[s >> 1] + j * kBBlock);
       }
-      if (s < 3) {
+      if constexpr (s < 3) {
 #pragma unroll
         for (int i = 0; i < WM; ++i) an[i] = *(const half8*)(st + a_off[s + 1] + i * 4096);
       }

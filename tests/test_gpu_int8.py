@@ -95,7 +95,9 @@ def test_int8_linear_ragged(gpu_lib, M, N):
 # register-fed kernel instead.  On the GPU's own fp16 x' the result differs
 # from the exact product only by the fp16 rounding of each decoded weight
 # (relative <= 2^-11) and fp32 accumulation.
-STAGED = [(4096, 2048, 512), (4000, 2100, 256), (4096, 2048, 128), (4096, 2049, 384)]
+STAGED = [(4096, 2048, 512), (4000, 2100, 256), (4096, 2048, 128), (4096, 2049, 384),
+          # narrow batches (M <= 64): one workgroup per 32 weight rows
+          (16, 4608, 3072), (64, 1000, 1024), (5, 33, 128)]
 
 
 @pytest.mark.parametrize("M,N,K", STAGED)
