@@ -225,6 +225,42 @@ def weight_only(rbp, torch, dev, stream, n=10):
     return res
 
 
+def video_layer(rbp, torch, dev, stream, n=10):
+    """The video-DiT projection (32768 tokens, 2048 -> 8192, h = 128, 64-level
+    activation and 16-level weight codebooks, W4A6): the fused rotate +
+    quantize and the decode GEMM, microseconds per launch with HBM GB/s and
+    TFLOP/s."""
+    import synth
+    inp = synth.make(5)
+    M, K, N = inp["M"], inp["K"], inp["N"]
+    to = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    X, W = to(inp["X"]), to(inp["W"])
+    rot = rbp.Rotation(inp["perm"], inp["signs"], inp["h"])
+    ca, cw = rbp.Codebook(K, inp["bits_a"]), rbp.Codebook(K, inp["bits_w"])
+    iw, r = rbp.pack_weights(rot, cw, W)
+    ia, s = rbp.quant_act(rot, ca, X)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        b.synchronize()
+        return a.elapsed_time(b) * 1e3 / n
+
+    tq = timed(lambda: rbp.quant_act(rot, ca, X))
+    tg = timed(lambda: rbp.qlinear(ia, s, ca, iw, r, cw, K, out=out))
+    qbytes = M * K * 2 + M * K * inp["bits_a"] // 8 + M * 4
+    return {"workload": "video-DiT projection W4A6: 32768 tokens, 2048 -> 8192, h = 128",
+            "quant_us": round(tq, 2), "quant_gbps": round(qbytes / tq / 1e3, 1),
+            "gemm_us": round(tg, 2), "gemm_tflops": round(2.0 * M * N * K / tg / 1e6, 1)}
+
+
 def source_digest(files):
     """sha256 over the kernel sources a traffic measurement was taken with."""
     import hashlib
@@ -398,6 +434,7 @@ def main():
     line["rotation_ablation"] = rotation_ablation(rbp, torch, dev, stream)
     line["mlp_pair"] = mlp_pair(rbp, torch, dev, stream)
     line["weight_only"] = weight_only(rbp, torch, dev, stream)
+    line["video_layer"] = video_layer(rbp, torch, dev, stream)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(line), flush=True)

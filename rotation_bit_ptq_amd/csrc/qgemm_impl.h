@@ -400,6 +400,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
   constexpr int STEPS = KC / 16;
   constexpr int kWM = WavesM<KIND>::value, kWN = 4 / kWM;  // wave grid
   constexpr int TM = 32 * WM * kWM, TN = 32 * WN * kWN;
+  static_assert(TM <= 256 && TN <= 256, "one thread per token and per weight row stages the factors");
   const uint32_t lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave % kWM, wn = wave / kWM;
@@ -985,7 +986,14 @@ hipError_t launch_shape(GemmArgs& g, int lds, hipStream_t stream) {
   if constexpr (kNarrow) {
     if (tiles(256, 192) >= 192) return launch_tile<KIND, OpA, OpB, 4, 3>(g, lds, stream);
   } else if constexpr (!(OpA::kLookups + OpB::kLookups >= 16 || (OpA::kBits == 8 && OpB::kBits == 3))) {
-    if (tiles(256, 128) >= 192) return launch_tile<KIND, OpA, OpB, 4, 2>(g, lds, stream);
+    // the operand with the costlier decode gets the shorter side of the wave
+    // tile: each of its blocks is decoded once per sub-step and feeds one
+    // MFMA per block of the other operand
+    if constexpr (KIND == 0 && OpA::kValu > OpB::kValu) {
+      if (tiles(128, 256) >= 192) return launch_tile<KIND, OpA, OpB, 2, 4>(g, lds, stream);
+    } else {
+      if (tiles(256, 128) >= 192) return launch_tile<KIND, OpA, OpB, 4, 2>(g, lds, stream);
+    }
   }
   if (tiles(128, 128) >= 128) return launch_tile<KIND, OpA, OpB, 2, 2>(g, lds, stream);
   return launch_tile<KIND, OpA, OpB, 1, 1>(g, lds, stream);

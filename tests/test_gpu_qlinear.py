@@ -110,27 +110,35 @@ def test_empty(gpu_lib):
     assert out.shape == (0, 4)
 
 
-def test_image_layer_full_size_sampled(gpu_lib):
-    """The image-DiT W4A4 layer at its full size (4096 x 3072 x 3072) in the
-    launch configuration the benchmark times; the oracle recomputes sampled
-    outputs and sampled tokens' codes one by one."""
+# (label, workload, act bits, weight bits): full-size layers in the launch
+# configurations the benchmark times.  The video layer and the wide-activation
+# pairs take the 2 x 4 wave tile (the costlier token decode on the short
+# side); the image and MLP layers the 4 x 3 tile.
+FULL = [("image-w4a4", 2, 4, 4), ("video-w4a6", 5, 6, 4), ("mlp-up-w2a4", 4, 4, 2),
+        ("image-w2a3", 2, 3, 2), ("image-w4a8", 2, 8, 4)]
+
+
+@pytest.mark.parametrize("label,cfg,ba,bw", FULL, ids=[c[0] for c in FULL])
+def test_layer_full_size_sampled(gpu_lib, label, cfg, ba, bw):
+    """A layer at its full size; the oracle recomputes sampled outputs and
+    sampled tokens' codes one by one."""
     rbp = gpu_lib
-    inp = synth.make(2)
+    inp = synth.make(cfg)
     K = inp["K"]
     _, ca, cw, ia, s, iw, r = _codes(rbp, inp["X"], inp["W"], inp["perm"], inp["signs"],
-                                     inp["h"], 4, 4)
+                                     inp["h"], ba, bw)
     out = rbp.qlinear(ia, s, ca, iw, r, cw, K)
     g = np.random.default_rng(0)
     ms = np.sort(g.choice(inp["M"], 48, replace=False))
     ns = np.sort(g.choice(inp["N"], 64, replace=False))
-    sub = _oracle_out(ia[ms], s[ms], iw[ns], r[ns], 4, 4, K)
+    sub = _oracle_out(ia[ms], s[ms], iw[ns], r[ns], ba, bw, K)
     got = out_f64(out[ms][:, ns])
-    assert rel_fro(got, sub) < OUT_TOL
+    assert rel_fro(got, sub) < OUT_TOL, label
     # the sampled tokens' codes against the oracle's rotation + quantizer
     from parity import check_indices
     ref = oracle.quant_act(as_f64(inp["X"][ms]), inp["perm"], inp["signs"], inp["h"],
-                           oracle.codebook(4), 4, synth.EPS)
-    check_indices(ia[ms], 4, K, ref["u"], oracle.codebook(4)["thresholds"], "full-size tokens")
+                           oracle.codebook(ba), ba, synth.EPS)
+    check_indices(ia[ms], ba, K, ref["u"], oracle.codebook(ba)["thresholds"], label)
 
 
 def test_deterministic(gpu_lib):
