@@ -6,30 +6,34 @@ namespace orbit {
 namespace qgemm {
 namespace {
 
-// Narrow batches (M <= 64 tokens, e.g. conditioning vectors): the product is
-// bound by the weight stream and by each wave's chain of dependent steps.
-// Each workgroup owns 32 weight rows and all tokens; its WV waves split K
-// (partial sums reduced in LDS), each keeps P chunks of 32 k in flight in a
-// register ring, and the two sub-steps of a chunk accumulate into separate
-// registers so consecutive MFMAs do not wait on each other.  The MFMA's
-// second operand holds the tokens (MB blocks of 32; rows past M re-read row
-// M - 1 and are dropped).
+// Narrow batches (M <= 32 tokens, e.g. conditioning vectors): the product is
+// bound by the weight stream.  Each workgroup owns 32 weight rows and all
+// tokens; its WV waves split K in groups of 128 (one scale group), reduced
+// in LDS.  Per group a lane reads whole cache lines: 64 (int8) or 32 (int4)
+// contiguous bytes of its weight row (the two halves of a row are adjacent)
+// and 128 contiguous bytes of each token row; the MFMA k order inside the
+// group is k = 64 half + 8 s + j for both operands (s = 0..7).  Each wave
+// keeps P groups in flight, and the sub-steps alternate between two
+// accumulators.  The MFMA's second operand holds the tokens (MB blocks of
+// 32; rows past M re-read row M - 1 and are dropped).
 template <class OpB, int MB, int WV, int P>
 __global__ __launch_bounds__(512) void narrow_kernel(GemmArgs g) {
-  __shared__ float red[WV - 1][MB][16][64];
+  constexpr int kWBytes = 64 * OpB::kCodeBits / 8;  // weight bytes per lane per group
+  constexpr int kWVec = kWBytes / 16;
+  __shared__ float red[WV > 1 ? WV - 1 : 1][MB][16][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r32 = lane & 31, half = lane >> 5;
   const long long n0 = (long long)blockIdx.x * 32;
   const long long nr = n0 + r32 < g.N ? n0 + r32 : g.N - 1;
-  const uint32_t ob = (uint32_t)(nr * g.ldb) + (uint32_t)(half * OpB::kBytes);
+  const uint32_t ob = (uint32_t)(nr * g.ldb) + (uint32_t)(half * kWBytes);
   const uint16_t* const srow = g.scale_f16 + nr * g.groups_per_row;
   uint32_t oa[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const long long m = 32 * mb + r32 < g.M ? 32 * mb + r32 : g.M - 1;
-    oa[mb] = (uint32_t)(m * g.lda) + (uint32_t)(half * F16Op::kBytes);
+    oa[mb] = (uint32_t)(m * g.lda) + (uint32_t)(half * 128);
   }
-  const int per = (int)(g.K / 32) / WV;  // chunks of this wave
+  const int per = g.groups_per_row / WV;  // groups of this wave
   const int c0 = wave * per, c1 = c0 + per, cm = c0 + (per / P) * P;
 
   floatx16 acc[2][MB];
@@ -39,26 +43,43 @@ __global__ __launch_bounds__(512) void narrow_kernel(GemmArgs g) {
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[s][mb][q] = 0.0f;
-  OpB wt[P];
-  F16Op tk[P][MB];
+  u32x4 wt[P][kWVec];
+  u32x4 tk[P][MB][8];
+  uint32_t sc[P];
   auto load = [&](int slot, int c) {
-    c = c < c1 ? c : c1 - 1;  // past the end: re-read the last chunk (unused)
-    wt[slot].load(g.b + ob + (uint32_t)c * (2u * OpB::kBytes));
-    const uint32_t sc = srow[(c * 32) >> 7];
-    wt[slot].scale2 = sc | (sc << 16);
+    c = c < c1 ? c : c1 - 1;  // past the end: re-read the last group (unused)
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) tk[slot][mb].load(g.a + oa[mb] + (uint32_t)c * 64u);
+    for (int v = 0; v < kWVec; ++v) wt[slot][v] = *(const u32x4*)(g.b + ob + (uint32_t)c * (2u * kWBytes) + 16u * v);
+    const uint32_t s16 = srow[c];
+    sc[slot] = s16 | (s16 << 16);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int v = 0; v < 8; ++v) tk[slot][mb][v] = *(const u32x4*)(g.a + oa[mb] + (uint32_t)c * 256u + 16u * v);
   };
   auto compute = [&](int slot) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const half8 bv = wt[slot].decode(s, 0);
+    for (int s = 0; s < 8; ++s) {
+      OpB op;
+      op.scale2 = sc[slot];
+      half8 bv;
+      if constexpr (OpB::kCodeBits == 8) {
+        const u32x4 w = wt[slot][s >> 1];
+        op.v = w;
+        bv = op.decode(s & 1, 0);
+      } else {
+        const u32x4 w = wt[slot][s >> 2];
+        const uint32_t d = (s & 3) == 0 ? w.x : (s & 3) == 1 ? w.y : (s & 3) == 2 ? w.z : w.w;
+        op.v = make_uint2(d, 0u);
+        bv = op.decode(0, 0);
+      }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
-        acc[s][mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bv, tk[slot][mb].decode(s, 0), acc[s][mb], 0, 0, 0);
+        acc[s & 1][mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+            bv, __builtin_bit_cast(half8, tk[slot][mb][s]), acc[s & 1][mb], 0, 0, 0);
     }
   };
-  // whole groups of P chunks through the ring, then the remaining chunks one
+  // whole rounds of P groups through the ring, then the remaining groups one
   // at a time
 #pragma unroll
   for (int p = 0; p < P; ++p) load(p, c0 + p);
@@ -104,28 +125,30 @@ __global__ __launch_bounds__(512) void narrow_kernel(GemmArgs g) {
   }
 }
 
-// Eight waves split K when it holds a multiple of eight chunks, else four.
+// Eight waves split K when it holds a multiple of eight groups, four when a
+// multiple of four, else one.
 template <class OpB, int MB>
 hipError_t launch_narrow(GemmArgs& g, hipStream_t stream) {
   const long long blocks = (g.N + 31) / 32;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  if ((g.K / 32) % 8 == 0)
-    hipLaunchKernelGGL((narrow_kernel<OpB, MB, 8, 4>), dim3((unsigned)blocks), dim3(512), 0, stream, g);
+  if (g.groups_per_row % 8 == 0)
+    hipLaunchKernelGGL((narrow_kernel<OpB, MB, 8, 2>), dim3((unsigned)blocks), dim3(512), 0, stream, g);
+  else if (g.groups_per_row % 4 == 0)
+    hipLaunchKernelGGL((narrow_kernel<OpB, MB, 4, 2>), dim3((unsigned)blocks), dim3(256), 0, stream, g);
   else
-    hipLaunchKernelGGL((narrow_kernel<OpB, MB, 4, 4>), dim3((unsigned)blocks), dim3(256), 0, stream, g);
+    hipLaunchKernelGGL((narrow_kernel<OpB, MB, 1, 2>), dim3((unsigned)blocks), dim3(64), 0, stream, g);
   return hipGetLastError();
 }
 
-// Narrow batches take the narrow kernel; large products the LDS-staged
-// kernel (256 x 256 tiles, a ring of three 64-k chunks); the rest the
-// register-fed kernel and its smaller tiles.  The staged kernel reads each
+// Narrow batches (up to 32 tokens) take the narrow kernel; large products
+// the LDS-staged kernel (256 x 256 tiles, a ring of three 64-k chunks); the
+// rest the register-fed kernel and its smaller tiles.  The staged kernel reads each
 // fp16 group scale through the aligned dword that holds it, so it also needs
 // a 4-byte aligned scale array with an even number of entries (else the last
 // dword would reach past the array).
 template <class OpB>
 hipError_t launch_weight_only(GemmArgs& g, hipStream_t stream) {
   if (g.M <= 32) return launch_narrow<OpB, 1>(g, stream);
-  if (g.M <= 64) return launch_narrow<OpB, 2>(g, stream);
   const long long tiles = ((g.M + 255) / 256) * ((g.N + 255) / 256);
   const bool scales_ok = ((uintptr_t)g.scale_f16 & 3) == 0 && (g.N * g.groups_per_row) % 2 == 0;
   if (tiles >= 128 && scales_ok) {

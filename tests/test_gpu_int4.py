@@ -132,7 +132,7 @@ def test_int4_rejects_bad_shapes(gpu_lib):
 # (4096, 2049, 384) has an odd number of scale entries and takes the
 # register-fed kernel instead.
 STAGED = [(4096, 2048, 512), (4000, 2100, 256), (4096, 2048, 128), (4096, 2049, 384),
-          # narrow batches (M <= 64): one workgroup per 32 weight rows
+          # narrow batches (M <= 32: one workgroup per 32 weight rows; 64: small tiles)
           (16, 4608, 3072), (64, 1000, 1024), (5, 33, 128)]
 
 

@@ -96,7 +96,7 @@ def test_int8_linear_ragged(gpu_lib, M, N):
 # from the exact product only by the fp16 rounding of each decoded weight
 # (relative <= 2^-11) and fp32 accumulation.
 STAGED = [(4096, 2048, 512), (4000, 2100, 256), (4096, 2048, 128), (4096, 2049, 384),
-          # narrow batches (M <= 64): one workgroup per 32 weight rows
+          # narrow batches (M <= 32: one workgroup per 32 weight rows; 64: small tiles)
           (16, 4608, 3072), (64, 1000, 1024), (5, 33, 128)]
 
 
