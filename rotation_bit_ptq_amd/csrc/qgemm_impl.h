@@ -355,9 +355,13 @@ __device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int& tm
 // Issue schedule of one sub-step: NMF MFMAs, each followed by its share of
 // the NDS LDS reads, NVA VALU instructions and NVM global loads, so the
 // matrix pipe is handed a new MFMA while the previous one is still running.
+// With eight or more MFMAs the reads go out behind the first NMF - 4 of
+// them: the last four (128 cycles of matrix work) cover the latency of the
+// last reads before the next sub-step waits for all of them.
 template <int NMF, int NDS, int NVA, int NVM, int K>
 __device__ __forceinline__ void issue_slot() {
-  constexpr int ds = NDS * (K + 1) / NMF - NDS * K / NMF;
+  constexpr int kReadSlots = NMF >= 8 ? NMF - 4 : NMF;
+  constexpr int ds = K < kReadSlots ? NDS * (K + 1) / kReadSlots - NDS * K / kReadSlots : 0;
   constexpr int va = NVA * (K + 1) / NMF - NVA * K / NMF;
   constexpr int vm = NVM * (K + 1) / NMF - NVM * K / NMF;
   __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
