@@ -15,21 +15,22 @@
 //     Rademacher sign of permuted coordinate k is part of its gather address:
 //       y_k = D_k x[pi(k)] = buf[pi(k) + (D_k < 0 ? d : 0)];
 //     the addresses are computed once per wave and stay in registers;
-//   * lane-slot j holds rotated coordinates 16 j .. 16 j + 15: for bf16 rows
-//     two gathered neighbours share a register and one v_dot2_f32_bf16 with
-//     (1, 1) or (1, -1) gives the first butterfly stage already in fp32; the
-//     next three stages run in registers and the remaining log2(h) - 4
-//     stages pair lanes j and j ^ 2^s through DPP moves (xor 1, 2, 8) or
-//     ds_swizzle (xor 4, 16);
-//   * the squared norm is reduced across the wave; the quantizer counts the
-//     thresholds below u with one lookup in a uniform grid over u: each cell
-//     holds at most one threshold, so idx = base[cell] + (t[cell] < u), the
-//     same float32 decision as a full count.  The cell index is read off the
-//     bits of fma(u, a, b + 2^23) (a monotone rounding), clamped by v_med3;
+//   * bf16 rows with h = 64, 128 or 256 use a transposed gather (TrShape
+//     below): every butterfly stage is a register add/sub, with one pass
+//     through a per-wave LDS scratch between H_T and H_16; other shapes
+//     gather 16 consecutive permuted coordinates per lane and pair lanes
+//     for the stages above 16 through DPP moves or ds_swizzle;
+//   * the squared norm comes from the loaded row (Pi is orthogonal) and is
+//     reduced across the wave; the quantizer counts the thresholds below u
+//     with one lookup in a uniform grid over u: each cell holds at most one
+//     threshold, so idx = base[cell] + (t[cell] < u), the same float32
+//     decision as a full count.  The cell index is read off the bits of
+//     fma(u, a, b + 2^23) (a monotone rounding), clamped by v_med3;
 //   * each lane writes its 16 codes as one 2*bits-byte word.
-// Rows with d <= 4096 keep their rotated values and gather addresses in
-// registers (one pass over LDS); longer rows make two passes (norm, then
-// quantize) over the LDS copy, so HBM is still read once.
+// Rows with d <= 4096 keep their gather addresses in registers (one pass
+// over LDS); longer rows take long_rows_kernel, one workgroup per row.  The
+// quantizing modes for bf16 rows with h = 128 and d = 1024 .. 4096 run the
+// Hadamard on the matrix cores instead (rpbh_mfma.h).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -890,6 +891,11 @@ hipError_t launch_fast_rounds(const RowArgs& a, hipStream_t stream) {
 
 template <int MODE, int LT>
 hipError_t launch_fast(const RowArgs& a, int bits, hipStream_t stream);
+
+// Matrix-core kernels (rpbh_mfma.h): bf16 rows, h = 128, d = 1024, 2048,
+// 3072 or 4096, codebook modes, code widths 2, 3, 4, 6 and 8.
+template <int MODE>
+hipError_t launch_mfma(const RowArgs& a, int bits, hipStream_t stream);
 
 #define ORBIT_ROWS_FAST(MODE, LT)                                             \
   template <>                                                               \

@@ -1,0 +1,258 @@
+// Rotate + quantize with the block Hadamard on the matrix cores: bf16 rows,
+// h = 128, d = 512 C (C = 2, 4, 6, 8), codebook modes (activations and
+// weights).
+//
+// OrbitQuant page, Method: x' = blkdiag(H_h D_i) P_pi x.  In Sylvester order
+// H_128 = H_4 (x) H_32: with position p = 32 t + r of a block (t < 4 groups
+// of r < 32), y_p = sum_t' H_4[t][t'] sum_r' H_32[r][r'] z_{32 t' + r'} for
+// the signed, permuted block z.  The inner sum over r' is a matrix product
+// Z (groups x 32) . H_32, run as v_mfma_f32_16x16x32_bf16 pairs: 16 groups
+// (4 blocks x 4 groups) times the two 32 x 16 halves of H_32.  Both factors
+// are exact in bf16 (z is a bf16 input with its sign flipped, H_32 is +-1)
+// and the products accumulate in fp32, so the result matches the fp32
+// butterflies up to rounding order.  The lane layout of that instruction
+// puts the 4 groups of one block, at columns r and r + 16, in one lane: H_4
+// is two register stages.  Against the butterfly kernels this removes the
+// bf16 widening, seven butterfly stages and the LDS transpose from every
+// coordinate.
+//
+// Per row (one wave, as in rows_kernel): the row lands once in the wave's
+// LDS buffer; each lane gathers 8 coordinates per MFMA pair (its A fragment:
+// permuted positions 8 (lane / 16) .. + 7 of group (lane % 16) % 4 of block
+// 4 c + (lane % 16) / 4) and flips their sign bits with masks kept in
+// registers; codes go to a per-wave byte buffer in position order and leave
+// as packed 16-code words, like the other row kernels.
+#pragma once
+
+#include "rpbh_impl.h"
+
+namespace orbit {
+namespace rows {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) const uint16_t lds_cu16_t;
+
+__device__ __forceinline__ uint32_t lds_read_u16(uint32_t addr) {
+  return *(lds_cu16_t*)(uintptr_t)addr;
+}
+
+// Sylvester-order Hadamard entry (-1)^popcount(i & j) as a bf16 bit pattern.
+__device__ __forceinline__ uint16_t hadamard_bf16(int i, int j) {
+  return (__builtin_popcount(i & j) & 1) ? 0xBF80u : 0x3F80u;
+}
+
+// Butterflies over the four groups (Sylvester order: spans 1 then 2).
+__device__ __forceinline__ void h4_stages(float& v0, float& v1, float& v2, float& v3) {
+  const float a0 = v0 + v1, a1 = v0 - v1, a2 = v2 + v3, a3 = v2 - v3;
+  v0 = a0 + a2;
+  v2 = a0 - a2;
+  v1 = a1 + a3;
+  v3 = a1 - a3;
+}
+
+// kX: also write the debug copy of x' (activation mode; a separate
+// instantiation, so the plain kernel carries none of its registers).
+template <int MODE, int BITS, int C, bool kX>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C <= 6 ? 3 : 2))) void mfma_rows_kernel(RowArgs a) {
+  static_assert(MODE == kAct || MODE == kWeight, "codebook modes only");
+  static_assert(C >= 1 && C <= 8, "rows of 512 C coordinates, C <= 8");
+  extern __shared__ __align__(16) char smem[];
+  constexpr int kD = 512 * C;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int waves = blockDim.x / kWave;
+  const uint32_t wbuf = (uint32_t)(a.grid_bytes + wave * a.wave_bytes);  // the row
+  const uint32_t cbuf = wbuf + 2u * kD;                                   // one code byte per position
+  const int r16 = lane & 15, kq = lane >> 4;
+  const long long stride = (long long)gridDim.x * waves;
+  long long row = (long long)blockIdx.x * waves + wave;
+
+  // B operands: the two column halves of H_32; lane holds k = 8 kq + j of
+  // column r16 (first half) and r16 + 16 (second half)
+  uint32_t hw0[4], hw1[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int k0 = 8 * kq + 2 * q;
+    hw0[q] = hadamard_bf16(k0, r16) | ((uint32_t)hadamard_bf16(k0 + 1, r16) << 16);
+    hw1[q] = hadamard_bf16(k0, r16 + 16) | ((uint32_t)hadamard_bf16(k0 + 1, r16 + 16) << 16);
+  }
+  const bf16x8 hb0 = __builtin_bit_cast(bf16x8, make_uint4(hw0[0], hw0[1], hw0[2], hw0[3]));
+  const bf16x8 hb1 = __builtin_bit_cast(bf16x8, make_uint4(hw1[0], hw1[1], hw1[2], hw1[3]));
+
+  // the first row's loads go out first; the loads of pi and the signs below
+  // overlap them
+  RowRegs<uint16_t, C> pre;
+  if (row < a.rows) pre.load(a, row, lane);
+
+  // gather offsets and sign masks: pair c, element j is permuted position
+  // k = 128 (4 c + r16 / 4) + 32 (r16 % 4) + 8 kq + j; y_k = D_k x[pi(k)]
+  // is the bf16 at wbuf + 2 pi(k) with its sign bit flipped when D_k < 0.
+  // Elements 2 q and 2 q + 1 share offset word q (16-bit byte offsets,
+  // low and high half) and mask word q.
+  uint32_t off[C][4], sgn[C][4];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int k0 = 128 * (4 * c + (r16 >> 2)) + 32 * (r16 & 3) + 8 * kq;
+    const i32x4 p0 = *(const i32x4*)(a.perm + k0), p1 = *(const i32x4*)(a.perm + k0 + 4);
+    const uint32_t sw = a.sign_bits[k0 >> 5] >> (k0 & 31);  // 8 signs (k0 % 8 == 0)
+    const int p[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      off[c][q] = ((uint32_t)p[2 * q] * 2u) | ((uint32_t)p[2 * q + 1] << 17);
+      sgn[c][q] = (((sw >> (2 * q)) & 1u) << 15) | (((sw >> (2 * q + 1)) & 1u) << 31);
+    }
+  }
+
+  build_grid(a, smem);
+  __syncthreads();
+  const float top = kMagic + (float)(a.cells - 1);
+  const floatx4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+
+  for (; row < a.rows; row += stride) {
+    const float ssx = pre.sumsq(a, lane);
+#pragma unroll
+    for (int j = 0; j < C; ++j) *(u32x4*)(smem + wbuf + (lane + kWave * j) * 16) = pre.c[j];
+    if (row + stride < a.rows) pre.load(a, row + stride, lane);
+    const float alpha = row_alpha<MODE, true>(a, wave_sum(ssx), row, lane);
+    wave_lds_sync();
+    // the 8 bf16 of pair c's A fragment, read into the low halves of lo and
+    // hi (the empty asm keeps the offsets packed: unpacked once outside the
+    // row loop they would take twice the registers)
+    auto gather = [&](int c, uint32_t (&lo)[4], uint32_t (&hi)[4]) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        asm volatile("" : "+v"(off[c][q]));
+        lo[q] = lds_read_u16(wbuf + (off[c][q] & 0xffffu));
+        hi[q] = lds_read_u16(wbuf + (off[c][q] >> 16));
+      }
+    };
+    float* const xr = kX ? a.xrot_f32 + row * kD : nullptr;
+    uint32_t lo[4], hi[4];
+    gather(0, lo, hi);
+    // pair c's grid cells are read at its end and used at the next pair's
+    // start, so their LDS latency hides behind that pair's gather and MFMAs
+    float u[8];
+    GridCell g[8];
+#pragma unroll
+    for (int c = 0; c <= C; ++c) {
+      float v[8];
+      if (c < C) {
+        // pair c + 1 is gathered while pair c is multiplied
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[q] = (lo[q] | (hi[q] << 16)) ^ sgn[c][q];
+        const bf16x8 av = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+        if (c + 1 < C) gather(c + 1, lo, hi);
+        const floatx4 y0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb0, zero, 0, 0, 0);
+        const floatx4 y1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb1, zero, 0, 0, 0);
+        // y0[i], y1[i]: group i of block 4 c + kq at columns r16, r16 + 16
+        v[0] = y0[0]; v[1] = y0[1]; v[2] = y0[2]; v[3] = y0[3];
+        v[4] = y1[0]; v[5] = y1[1]; v[6] = y1[2]; v[7] = y1[3];
+      }
+      if (c > 0) {  // the codes of pair c - 1
+        const int base = 128 * (4 * (c - 1) + kq) + r16;  // position of element 0
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          smem[cbuf + base + 32 * (e & 3) + 16 * (e >> 2)] = (char)(g[e].base + (g[e].t < u[e] ? 1 : 0));
+      }
+      if (c < C) {
+        h4_stages(v[0], v[1], v[2], v[3]);
+        h4_stages(v[4], v[5], v[6], v[7]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          u[e] = v[e] * alpha;
+          g[e] = *(const GridCell*)(smem + grid_addr(u[e], a.ga, a.gb, top, a.grid_bias));
+        }
+        if constexpr (kX) {
+          const int base = 128 * (4 * c + kq) + r16;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xr[base + 32 * (e & 3) + 16 * (e >> 2)] = v[e] * a.inv_sqrt_h;
+        }
+      }
+      // one pair at a time: hoisting later gathers would hold their
+      // registers and cost occupancy
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wave_lds_sync();  // the row's codes are in the byte buffer
+    uint8_t* const out = a.idx_out + (size_t)row * ((size_t)kD * BITS / 8);
+#pragma unroll
+    for (int s = 0; s < C / 2; ++s) {  // 32 C slots of 16 codes: C / 2 per lane
+      const int slot = s * kWave + lane;
+      const u32x4 cw = *(const u32x4*)(smem + cbuf + slot * 16);
+      const uint32_t ww[4] = {cw.x, cw.y, cw.z, cw.w};
+      int idx[kSlot];
+#pragma unroll
+      for (int i = 0; i < kSlot; ++i) idx[i] = (int)((ww[i >> 2] >> (8 * (i & 3))) & 0xffu);
+      store_indices<BITS>(out, slot, idx);
+    }
+    wave_lds_sync();  // every lane has read its gathers and codes before the next row lands
+  }
+}
+
+// LDS bytes per wave: the bf16 row and its code bytes.
+template <int C>
+constexpr int mfma_wave_bytes() { return 3 * 512 * C; }
+
+template <int MODE, int BITS, int C, bool kX>
+hipError_t launch_mfma_typed(RowArgs a, hipStream_t stream) {
+  DeviceInfo di;
+  hipError_t e = device_info(&di);
+  if (e != hipSuccess) return e;
+  a.wave_bytes = mfma_wave_bytes<C>();
+  int waves = 4;
+  while (waves > 1 && a.grid_bytes + waves * a.wave_bytes > di.max_lds) waves >>= 1;
+  const int lds = a.grid_bytes + waves * a.wave_bytes;
+  if (lds > di.max_lds) return hipErrorInvalidValue;
+  auto kern = mfma_rows_kernel<MODE, BITS, C, kX>;
+  static LaunchCache cache;
+  int per_cu = 1;
+  e = prepare_launch(cache, (const void*)kern, waves * kWave, lds, &per_cu);
+  if (e != hipSuccess) return e;
+  const long long need = (a.rows + waves - 1) / waves;
+  const long long cap = (long long)di.n_cu * per_cu;
+  const int blocks = (int)(need < cap ? need : cap);
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(waves * kWave), lds, stream, a);
+  return hipGetLastError();
+}
+
+template <int MODE, int BITS, bool kX>
+hipError_t launch_mfma_d(const RowArgs& a, hipStream_t stream) {
+  switch (a.d) {
+    case 1024: return launch_mfma_typed<MODE, BITS, 2, kX>(a, stream);
+    case 2048: return launch_mfma_typed<MODE, BITS, 4, kX>(a, stream);
+    case 3072: return launch_mfma_typed<MODE, BITS, 6, kX>(a, stream);
+    case 4096: return launch_mfma_typed<MODE, BITS, 8, kX>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int MODE, int BITS>
+hipError_t launch_mfma_bits(const RowArgs& a, hipStream_t stream) {
+  if constexpr (MODE == kAct) {
+    if (a.xrot_f32) return launch_mfma_d<MODE, BITS, true>(a, stream);
+  }
+  return launch_mfma_d<MODE, BITS, false>(a, stream);
+}
+
+}  // namespace rows
+}  // namespace orbit
+
+namespace orbit {
+namespace rows {
+
+#define ORBIT_ROWS_MFMA(MODE)                                                   \
+  template <>                                                                 \
+  hipError_t launch_mfma<MODE>(const RowArgs& a, int bits, hipStream_t s) {   \
+    switch (bits) {                                                           \
+      case 2: return launch_mfma_bits<MODE, 2>(a, s);                         \
+      case 3: return launch_mfma_bits<MODE, 3>(a, s);                         \
+      case 4: return launch_mfma_bits<MODE, 4>(a, s);                         \
+      case 6: return launch_mfma_bits<MODE, 6>(a, s);                         \
+      case 8: return launch_mfma_bits<MODE, 8>(a, s);                         \
+    }                                                                         \
+    return hipErrorInvalidValue;                                              \
+  }
+
+}  // namespace rows
+}  // namespace orbit

@@ -1,0 +1,8 @@
+// Matrix-core rotate + quantize kernels: bf16 weight rows, h = 128 (see rpbh_mfma.h).
+#include "rpbh_mfma.h"
+
+namespace orbit {
+namespace rows {
+ORBIT_ROWS_MFMA(kWeight)
+}  // namespace rows
+}  // namespace orbit
