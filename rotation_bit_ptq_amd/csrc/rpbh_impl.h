@@ -892,9 +892,9 @@ hipError_t launch_fast_rounds(const RowArgs& a, hipStream_t stream) {
 template <int MODE, int LT>
 hipError_t launch_fast(const RowArgs& a, int bits, hipStream_t stream);
 
-// Matrix-core kernels (rpbh_mfma.h): bf16 rows, h = 128, d = 1024, 2048,
-// 3072 or 4096, codebook modes, code widths 2, 3, 4, 6 and 8.
-template <int MODE>
+// Matrix-core kernels (rpbh_mfma.h): bf16 rows, h = 32 G (64, 128, 256),
+// d = 1024, 2048, 3072 or 4096, codebook modes, code widths 2, 3, 4, 6, 8.
+template <int MODE, int G>
 hipError_t launch_mfma(const RowArgs& a, int bits, hipStream_t stream);
 
 #define ORBIT_ROWS_FAST(MODE, LT)                                             \

@@ -1,20 +1,22 @@
 // Rotate + quantize with the block Hadamard on the matrix cores: bf16 rows,
-// h = 128, d = 512 C (C = 2, 4, 6, 8), codebook modes (activations and
-// weights).
+// h = 32 G (G = 2, 4, 8: h = 64, 128, 256), d = 512 C (C = 2, 4, 6, 8),
+// codebook modes (activations and weights).
 //
 // OrbitQuant page, Method: x' = blkdiag(H_h D_i) P_pi x.  In Sylvester order
-// H_128 = H_4 (x) H_32: with position p = 32 t + r of a block (t < 4 groups
-// of r < 32), y_p = sum_t' H_4[t][t'] sum_r' H_32[r][r'] z_{32 t' + r'} for
-// the signed, permuted block z.  The inner sum over r' is a matrix product
+// H_h = H_G (x) H_32: with position p = 32 t + r of a block (t < G groups of
+// r < 32), y_p = sum_t' H_G[t][t'] sum_r' H_32[r][r'] z_{32 t' + r'} for the
+// signed, permuted block z.  The inner sum over r' is a matrix product
 // Z (groups x 32) . H_32, run as v_mfma_f32_16x16x32_bf16 pairs: 16 groups
-// (4 blocks x 4 groups) times the two 32 x 16 halves of H_32.  Both factors
-// are exact in bf16 (z is a bf16 input with its sign flipped, H_32 is +-1)
-// and the products accumulate in fp32, so the result matches the fp32
-// butterflies up to rounding order.  The lane layout of that instruction
-// puts the 4 groups of one block, at columns r and r + 16, in one lane: H_4
-// is two register stages.  Against the butterfly kernels this removes the
-// bf16 widening, seven butterfly stages and the LDS transpose from every
-// coordinate.
+// (16 / G blocks of G groups) times the two 32 x 16 halves of H_32.  Both
+// factors are exact in bf16 (z is a bf16 input with its sign flipped, H_32
+// is +-1) and the products accumulate in fp32, so the result matches the
+// fp32 butterflies up to rounding order.  The lane layout of that
+// instruction gives lane l the 4 consecutive groups 4 (l / 16) .. + 3 of the
+// pair, at columns r and r + 16: H_G is register stages over those 4
+// groups (two stages for G = 4, one for G = 2) and, for G = 8, one more
+// stage between lanes l and l ^ 16.  Against the butterfly kernels this
+// removes the bf16 widening, five of the log2(h) butterfly stages and the
+// LDS transpose from every coordinate.
 //
 // Per row (one wave, as in rows_kernel): the row lands once in the wave's
 // LDS buffer; each lane gathers 8 coordinates per MFMA pair (its A fragment:
@@ -42,21 +44,28 @@ __device__ __forceinline__ uint16_t hadamard_bf16(int i, int j) {
   return (__builtin_popcount(i & j) & 1) ? 0xBF80u : 0x3F80u;
 }
 
-// Butterflies over the four groups (Sylvester order: spans 1 then 2).
-__device__ __forceinline__ void h4_stages(float& v0, float& v1, float& v2, float& v3) {
+// Butterflies over a lane's four consecutive groups: span 1, and span 2
+// when a block has 4 or more groups.
+template <int G>
+__device__ __forceinline__ void group_stages(float& v0, float& v1, float& v2, float& v3) {
   const float a0 = v0 + v1, a1 = v0 - v1, a2 = v2 + v3, a3 = v2 - v3;
-  v0 = a0 + a2;
-  v2 = a0 - a2;
-  v1 = a1 + a3;
-  v3 = a1 - a3;
+  if constexpr (G == 2) {
+    v0 = a0; v1 = a1; v2 = a2; v3 = a3;
+  } else {
+    v0 = a0 + a2;
+    v2 = a0 - a2;
+    v1 = a1 + a3;
+    v3 = a1 - a3;
+  }
 }
 
 // kX: also write the debug copy of x' (activation mode; a separate
 // instantiation, so the plain kernel carries none of its registers).
-template <int MODE, int BITS, int C, bool kX>
+template <int MODE, int BITS, int G, int C, bool kX>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C <= 6 ? 3 : 2))) void mfma_rows_kernel(RowArgs a) {
   static_assert(MODE == kAct || MODE == kWeight, "codebook modes only");
   static_assert(C >= 1 && C <= 8, "rows of 512 C coordinates, C <= 8");
+  static_assert(G == 2 || G == 4 || G == 8, "h = 64, 128 or 256");
   extern __shared__ __align__(16) char smem[];
   constexpr int kD = 512 * C;
   const int lane = threadIdx.x & (kWave - 1);
@@ -85,15 +94,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C <= 6 ? 3 
   RowRegs<uint16_t, C> pre;
   if (row < a.rows) pre.load(a, row, lane);
 
-  // gather offsets and sign masks: pair c, element j is permuted position
-  // k = 128 (4 c + r16 / 4) + 32 (r16 % 4) + 8 kq + j; y_k = D_k x[pi(k)]
+  // gather offsets and sign masks.  Pair c covers positions 512 c .. + 511
+  // (16 / G whole blocks), group rho = 16 c + (position % 512) / 32 being A
+  // row rho % 16; element j of the lane's fragment is permuted position
+  // k = 512 c + 32 r16 + 8 kq + j, for any G; y_k = D_k x[pi(k)]
   // is the bf16 at wbuf + 2 pi(k) with its sign bit flipped when D_k < 0.
   // Elements 2 q and 2 q + 1 share offset word q (16-bit byte offsets,
   // low and high half) and mask word q.
   uint32_t off[C][4], sgn[C][4];
 #pragma unroll
   for (int c = 0; c < C; ++c) {
-    const int k0 = 128 * (4 * c + (r16 >> 2)) + 32 * (r16 & 3) + 8 * kq;
+    const int k0 = 512 * c + 32 * r16 + 8 * kq;
     const i32x4 p0 = *(const i32x4*)(a.perm + k0), p1 = *(const i32x4*)(a.perm + k0 + 4);
     const uint32_t sw = a.sign_bits[k0 >> 5] >> (k0 & 31);  // 8 signs (k0 % 8 == 0)
     const int p[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
@@ -146,26 +157,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C <= 6 ? 3 
         if (c + 1 < C) gather(c + 1, lo, hi);
         const floatx4 y0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb0, zero, 0, 0, 0);
         const floatx4 y1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb1, zero, 0, 0, 0);
-        // y0[i], y1[i]: group i of block 4 c + kq at columns r16, r16 + 16
+        // y0[i], y1[i]: A row 4 kq + i at columns r16 and r16 + 16, i.e.
+        // positions 512 c + 128 kq + 32 i + r16 (+ 16)
         v[0] = y0[0]; v[1] = y0[1]; v[2] = y0[2]; v[3] = y0[3];
         v[4] = y1[0]; v[5] = y1[1]; v[6] = y1[2]; v[7] = y1[3];
       }
       if (c > 0) {  // the codes of pair c - 1
-        const int base = 128 * (4 * (c - 1) + kq) + r16;  // position of element 0
+        const int base = 512 * (c - 1) + 128 * kq + r16;  // position of element 0
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           smem[cbuf + base + 32 * (e & 3) + 16 * (e >> 2)] = (char)(g[e].base + (g[e].t < u[e] ? 1 : 0));
       }
       if (c < C) {
-        h4_stages(v[0], v[1], v[2], v[3]);
-        h4_stages(v[4], v[5], v[6], v[7]);
+        group_stages<G>(v[0], v[1], v[2], v[3]);
+        group_stages<G>(v[4], v[5], v[6], v[7]);
+        if constexpr (G == 8) {  // groups t and t ^ 4 sit in lanes l and l ^ 16
+#pragma clang fp contract(off)
+          const float sg = (lane & 16) ? -1.0f : 1.0f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = xor_partner<16>(v[e]) + v[e] * sg;
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           u[e] = v[e] * alpha;
           g[e] = *(const GridCell*)(smem + grid_addr(u[e], a.ga, a.gb, top, a.grid_bias));
         }
         if constexpr (kX) {
-          const int base = 128 * (4 * c + kq) + r16;
+          const int base = 512 * c + 128 * kq + r16;
 #pragma unroll
           for (int e = 0; e < 8; ++e) xr[base + 32 * (e & 3) + 16 * (e >> 2)] = v[e] * a.inv_sqrt_h;
         }
@@ -194,7 +212,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C <= 6 ? 3 
 template <int C>
 constexpr int mfma_wave_bytes() { return 3 * 512 * C; }
 
-template <int MODE, int BITS, int C, bool kX>
+template <int MODE, int BITS, int G, int C, bool kX>
 hipError_t launch_mfma_typed(RowArgs a, hipStream_t stream) {
   DeviceInfo di;
   hipError_t e = device_info(&di);
@@ -204,7 +222,7 @@ hipError_t launch_mfma_typed(RowArgs a, hipStream_t stream) {
   while (waves > 1 && a.grid_bytes + waves * a.wave_bytes > di.max_lds) waves >>= 1;
   const int lds = a.grid_bytes + waves * a.wave_bytes;
   if (lds > di.max_lds) return hipErrorInvalidValue;
-  auto kern = mfma_rows_kernel<MODE, BITS, C, kX>;
+  auto kern = mfma_rows_kernel<MODE, BITS, G, C, kX>;
   static LaunchCache cache;
   int per_cu = 1;
   e = prepare_launch(cache, (const void*)kern, waves * kWave, lds, &per_cu);
@@ -216,24 +234,26 @@ hipError_t launch_mfma_typed(RowArgs a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int MODE, int BITS, bool kX>
+template <int MODE, int BITS, int G, bool kX>
 hipError_t launch_mfma_d(const RowArgs& a, hipStream_t stream) {
   switch (a.d) {
-    case 1024: return launch_mfma_typed<MODE, BITS, 2, kX>(a, stream);
-    case 2048: return launch_mfma_typed<MODE, BITS, 4, kX>(a, stream);
-    case 3072: return launch_mfma_typed<MODE, BITS, 6, kX>(a, stream);
-    case 4096: return launch_mfma_typed<MODE, BITS, 8, kX>(a, stream);
+    case 1024: return launch_mfma_typed<MODE, BITS, G, 2, kX>(a, stream);
+    case 2048: return launch_mfma_typed<MODE, BITS, G, 4, kX>(a, stream);
+    case 3072: return launch_mfma_typed<MODE, BITS, G, 6, kX>(a, stream);
+    case 4096: return launch_mfma_typed<MODE, BITS, G, 8, kX>(a, stream);
   }
   return hipErrorInvalidValue;
 }
 
-template <int MODE, int BITS>
-hipError_t launch_mfma_bits(const RowArgs& a, hipStream_t stream) {
+template <int MODE, int BITS, int G>
+hipError_t launch_mfma_h(const RowArgs& a, hipStream_t stream) {
   if constexpr (MODE == kAct) {
-    if (a.xrot_f32) return launch_mfma_d<MODE, BITS, true>(a, stream);
+    if (a.xrot_f32) return launch_mfma_d<MODE, BITS, G, true>(a, stream);
   }
-  return launch_mfma_d<MODE, BITS, false>(a, stream);
+  return launch_mfma_d<MODE, BITS, G, false>(a, stream);
 }
+
+
 
 }  // namespace rows
 }  // namespace orbit
@@ -241,17 +261,17 @@ hipError_t launch_mfma_bits(const RowArgs& a, hipStream_t stream) {
 namespace orbit {
 namespace rows {
 
-#define ORBIT_ROWS_MFMA(MODE)                                                   \
-  template <>                                                                 \
-  hipError_t launch_mfma<MODE>(const RowArgs& a, int bits, hipStream_t s) {   \
-    switch (bits) {                                                           \
-      case 2: return launch_mfma_bits<MODE, 2>(a, s);                         \
-      case 3: return launch_mfma_bits<MODE, 3>(a, s);                         \
-      case 4: return launch_mfma_bits<MODE, 4>(a, s);                         \
-      case 6: return launch_mfma_bits<MODE, 6>(a, s);                         \
-      case 8: return launch_mfma_bits<MODE, 8>(a, s);                         \
-    }                                                                         \
-    return hipErrorInvalidValue;                                              \
+#define ORBIT_ROWS_MFMA(MODE, G)                                                 \
+  template <>                                                                  \
+  hipError_t launch_mfma<MODE, G>(const RowArgs& a, int bits, hipStream_t s) { \
+    switch (bits) {                                                            \
+      case 2: return launch_mfma_h<MODE, 2, G>(a, s);                          \
+      case 3: return launch_mfma_h<MODE, 3, G>(a, s);                          \
+      case 4: return launch_mfma_h<MODE, 4, G>(a, s);                          \
+      case 6: return launch_mfma_h<MODE, 6, G>(a, s);                          \
+      case 8: return launch_mfma_h<MODE, 8, G>(a, s);                          \
+    }                                                                          \
+    return hipErrorInvalidValue;                                               \
   }
 
 }  // namespace rows

@@ -3,6 +3,6 @@
 
 namespace orbit {
 namespace rows {
-ORBIT_ROWS_MFMA(kAct)
+ORBIT_ROWS_MFMA(kAct, 4)
 }  // namespace rows
 }  // namespace orbit

@@ -1,0 +1,8 @@
+// Matrix-core rotate + quantize kernels: bf16 activation rows, h = 256 (see rpbh_mfma.h).
+#include "rpbh_mfma.h"
+
+namespace orbit {
+namespace rows {
+ORBIT_ROWS_MFMA(kAct, 8)
+}  // namespace rows
+}  // namespace orbit

@@ -3,6 +3,6 @@
 
 namespace orbit {
 namespace rows {
-ORBIT_ROWS_MFMA(kWeight)
+ORBIT_ROWS_MFMA(kWeight, 4)
 }  // namespace rows
 }  // namespace orbit

@@ -68,12 +68,14 @@ hipError_t launch_rows(const RowJob& job, hipStream_t stream) {
   // the gather plan serves the kernels whose gather order it was built in
   // (transposed exactly when h allows it)
   if (job.gather && fast == tr_order) a.gather = job.gather;
-  // bf16 rows with h = 128 and d = 1024, 2048, 3072 or 4096, codebook modes:
-  // the Hadamard runs on the matrix cores
-  const bool mfma = fast && quant && job.h == 128 && job.d % 1024 == 0 && job.d <= 4096;
+  // bf16 rows with h = 64, 128 or 256 and d = 1024, 2048, 3072 or 4096,
+  // codebook modes: the Hadamard runs on the matrix cores
+  const bool mfma = fast && quant && job.d % 1024 == 0 && job.d <= 4096;
   if (mfma) {
-    if (job.mode == RowMode::kActQuant) return launch_mfma<kAct>(a, job.bits, stream);
-    return launch_mfma<kWeight>(a, job.bits, stream);
+    const bool act = job.mode == RowMode::kActQuant;
+    if (job.h == 64) return act ? launch_mfma<kAct, 2>(a, job.bits, stream) : launch_mfma<kWeight, 2>(a, job.bits, stream);
+    if (job.h == 128) return act ? launch_mfma<kAct, 4>(a, job.bits, stream) : launch_mfma<kWeight, 4>(a, job.bits, stream);
+    return act ? launch_mfma<kAct, 8>(a, job.bits, stream) : launch_mfma<kWeight, 8>(a, job.bits, stream);
   }
   if (fast) {
     const int lt = job.h == 64 ? 2 : (job.h == 128 ? 3 : 4);

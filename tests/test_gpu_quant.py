@@ -83,6 +83,35 @@ def test_quant_act_shapes(gpu_lib, d, h):
     _run_act(gpu_lib, X, perm, signs, h, 4, f"d{d}-h{h}")
 
 
+# bf16 rows with h = 64, 128, 256 and d = 1024 .. 4096 take the matrix-core
+# kernels (H_32 as bf16 MFMAs, the group stages in registers and, for
+# h = 256, between lanes l and l ^ 16); 77 rows leave waves without a row
+@pytest.mark.parametrize("d,h,bits", [(1024, 64, 4), (2048, 256, 2), (4096, 256, 6), (4096, 64, 8),
+                                      (3072, 256, 3), (2048, 128, 8), (1024, 256, 4)])
+def test_quant_act_matrix_core_shapes(gpu_lib, d, h, bits):
+    perm, signs = synth.rotation_params(d, 7 * d + h)
+    g = np.random.default_rng(d + 3 * h + bits)
+    X = synth.f32_to_bf16_bits(g.standard_normal((77, d)).astype(np.float32))
+    X[11] = 0
+    _run_act(gpu_lib, X, perm, signs, h, bits, f"mfma-d{d}-h{h}-a{bits}")
+
+
+@pytest.mark.parametrize("d,h", [(1024, 64), (4096, 256)])
+def test_weight_pack_matrix_core_shapes(gpu_lib, d, h):
+    rbp = gpu_lib
+    perm, signs = synth.rotation_params(d, 5 * d + h)
+    g = np.random.default_rng(d + h)
+    W = synth.f32_to_bf16_bits((0.03 * g.standard_normal((90, d))).astype(np.float32))
+    rot = rbp.Rotation(perm, signs, h)
+    cb = rbp.Codebook(d, 2)
+    ref_cb = oracle.codebook(2)
+    idx, r = rbp.pack_weights(rot, cb, to_dev(W))
+    ref = oracle.pack_weights(as_f64(W), perm, signs, h, ref_cb, 2)
+    check_indices(idx, 2, d, ref["u"], ref_cb["thresholds"], f"mfma-w-d{d}-h{h}")
+    diff = np.abs(bits_of(r).astype(np.int64) - ref["r_bf16"].astype(np.int64))
+    assert np.all(diff <= 1)
+
+
 @pytest.mark.parametrize("d", [2048, 4096])
 def test_full_rht_rotate_and_weights(gpu_lib, d):
     """Full RHT (OrbitQuant page, Experiments: the rotation ablation), h = d:
