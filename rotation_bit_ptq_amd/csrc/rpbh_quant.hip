@@ -69,8 +69,17 @@ hipError_t launch_rows(const RowJob& job, hipStream_t stream) {
   // (transposed exactly when h allows it)
   if (job.gather && fast == tr_order) a.gather = job.gather;
   // bf16 rows with h = 64, 128 or 256 and d = 1024, 2048, 3072 or 4096,
-  // codebook modes: the Hadamard runs on the matrix cores
-  const bool mfma = fast && quant && job.d % 1024 == 0 && job.d <= 4096;
+  // codebook modes: the Hadamard runs on the matrix cores.  Measured on
+  // MI355X, the matrix-core kernel costs less per row but more to start a
+  // wave, and with 3072-wide rows (three waves per SIMD) it only wins once
+  // there are more than 16 rows per compute unit.
+  bool mfma = fast && quant && job.d % 1024 == 0 && job.d <= 4096;
+  if (mfma && job.d == 3072) {
+    DeviceInfo di;
+    const hipError_t e = device_info(&di);
+    if (e != hipSuccess) return e;
+    mfma = job.rows > 16LL * di.n_cu;
+  }
   if (mfma) {
     const bool act = job.mode == RowMode::kActQuant;
     if (job.h == 64) return act ? launch_mfma<kAct, 2>(a, job.bits, stream) : launch_mfma<kWeight, 2>(a, job.bits, stream);

@@ -96,6 +96,15 @@ def test_quant_act_matrix_core_shapes(gpu_lib, d, h, bits):
     _run_act(gpu_lib, X, perm, signs, h, bits, f"mfma-d{d}-h{h}-a{bits}")
 
 
+def test_quant_act_matrix_core_3072_wide(gpu_lib):
+    # 3072-wide rows take the matrix-core kernel above 16 rows per compute
+    # unit (4096 on MI355X): 4100 rows, a ragged last round of waves
+    g = np.random.default_rng(41)
+    perm, signs = synth.rotation_params(3072, 41)
+    X = synth.f32_to_bf16_bits(g.standard_normal((4100, 3072)).astype(np.float32))
+    _run_act(gpu_lib, X, perm, signs, 128, 4, "mfma-d3072-4100rows")
+
+
 @pytest.mark.parametrize("d,h", [(1024, 64), (4096, 256)])
 def test_weight_pack_matrix_core_shapes(gpu_lib, d, h):
     rbp = gpu_lib
