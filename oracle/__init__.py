@@ -21,7 +21,7 @@ It is written as a plain, slow, direct reading of the pages, in float64:
   Its 4-bit sibling (``int4``) stands for the INT4 projections the OrbitQuant
   page's Experiments section favours in its ablations.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
 Hadamard matrices are Sylvester-ordered and orthonormal (H_h / sqrt(h));
 P_pi gathers, (P_pi x)_k = x[pi(k)]; the signs D act on the permuted index;
 the codebook is stored in N(0,1) units (the N(0,1/d) codebook is it divided
