@@ -1,6 +1,6 @@
 // Rotate + quantize with the block Hadamard on the matrix cores: bf16 rows,
 // h = 32 G (G = 2, 4, 8: h = 64, 128, 256), d = 512 C (C = 2, 4, 6, 8),
-// codebook modes (activations and weights).
+// codebook modes (activations and weights) and the fp16 rotation.
 //
 // OrbitQuant page, Method: x' = blkdiag(H_h D_i) P_pi x.  In Sylvester order
 // H_h = H_G (x) H_32: with position p = 32 t + r of a block (t < G groups of
@@ -63,7 +63,8 @@ __device__ __forceinline__ void group_stages(float& v0, float& v1, float& v2, fl
 // instantiation, so the plain kernel carries none of its registers).
 template <int MODE, int BITS, int G, int C, bool kX>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C <= 6 ? 3 : 2))) void mfma_rows_kernel(RowArgs a) {
-  static_assert(MODE == kAct || MODE == kWeight, "codebook modes only");
+  static_assert(MODE == kAct || MODE == kWeight || MODE == kRotF16, "codebook modes and fp16 x'");
+  constexpr bool kQuant = MODE != kRotF16;
   static_assert(C >= 1 && C <= 8, "rows of 512 C coordinates, C <= 8");
   static_assert(G == 2 || G == 4 || G == 8, "h = 64, 128 or 256");
   extern __shared__ __align__(16) char smem[];
@@ -72,7 +73,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C <= 6 ? 3 
   const int wave = threadIdx.x / kWave;
   const int waves = blockDim.x / kWave;
   const uint32_t wbuf = (uint32_t)(a.grid_bytes + wave * a.wave_bytes);  // the row
-  const uint32_t cbuf = wbuf + 2u * kD;                                   // one code byte per position
+  const uint32_t cbuf = wbuf + 2u * kD;  // one code byte (fp16 x' for kRotF16) per position
   const int r16 = lane & 15, kq = lane >> 4;
   const long long stride = (long long)gridDim.x * waves;
   long long row = (long long)blockIdx.x * waves + wave;
@@ -115,17 +116,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C <= 6 ? 3 
     }
   }
 
-  build_grid(a, smem);
+  if constexpr (kQuant) build_grid(a, smem);
   __syncthreads();
   const float top = kMagic + (float)(a.cells - 1);
   const floatx4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
 
   for (; row < a.rows; row += stride) {
-    const float ssx = pre.sumsq(a, lane);
+    float ssx = 0.0f;
+    if constexpr (kQuant) ssx = pre.sumsq(a, lane);
 #pragma unroll
     for (int j = 0; j < C; ++j) *(u32x4*)(smem + wbuf + (lane + kWave * j) * 16) = pre.c[j];
     if (row + stride < a.rows) pre.load(a, row + stride, lane);
-    const float alpha = row_alpha<MODE, true>(a, wave_sum(ssx), row, lane);
+    float alpha = 0.0f;
+    if constexpr (kQuant) alpha = row_alpha<MODE, true>(a, wave_sum(ssx), row, lane);
     wave_lds_sync();
     // the 8 bf16 of pair c's A fragment, read into the low halves of lo and
     // hi (the empty asm keeps the offsets packed: unpacked once outside the
@@ -162,7 +165,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C <= 6 ? 3 
         v[0] = y0[0]; v[1] = y0[1]; v[2] = y0[2]; v[3] = y0[3];
         v[4] = y1[0]; v[5] = y1[1]; v[6] = y1[2]; v[7] = y1[3];
       }
-      if (c > 0) {  // the codes of pair c - 1
+      if (kQuant && c > 0) {  // the codes of pair c - 1
         const int base = 512 * (c - 1) + 128 * kq + r16;  // position of element 0
 #pragma unroll
         for (int e = 0; e < 8; ++e)
@@ -177,47 +180,61 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C <= 6 ? 3 
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = xor_partner<16>(v[e]) + v[e] * sg;
         }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          u[e] = v[e] * alpha;
-          g[e] = *(const GridCell*)(smem + grid_addr(u[e], a.ga, a.gb, top, a.grid_bias));
-        }
-        if constexpr (kX) {
+        if constexpr (!kQuant) {  // fp16 x' into the staging buffer
           const int base = 512 * c + 128 * kq + r16;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) xr[base + 32 * (e & 3) + 16 * (e >> 2)] = v[e] * a.inv_sqrt_h;
+          for (int e = 0; e < 8; ++e)
+            *(uint16_t*)(smem + cbuf + 2 * (base + 32 * (e & 3) + 16 * (e >> 2))) = f32_to_f16_rne(v[e] * a.inv_sqrt_h);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            u[e] = v[e] * alpha;
+            g[e] = *(const GridCell*)(smem + grid_addr(u[e], a.ga, a.gb, top, a.grid_bias));
+          }
+          if constexpr (kX) {
+            const int base = 512 * c + 128 * kq + r16;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xr[base + 32 * (e & 3) + 16 * (e >> 2)] = v[e] * a.inv_sqrt_h;
+          }
         }
       }
       // one pair at a time: hoisting later gathers would hold their
       // registers and cost occupancy
       __builtin_amdgcn_sched_barrier(0);
     }
-    wave_lds_sync();  // the row's codes are in the byte buffer
-    uint8_t* const out = a.idx_out + (size_t)row * ((size_t)kD * BITS / 8);
+    wave_lds_sync();  // the row's codes (or fp16 x') are in the staging buffer
+    if constexpr (!kQuant) {  // 64 C pieces of 16 bytes: C per lane
+      uint4* const out = (uint4*)(a.xrot_f16 + (size_t)row * kD);
 #pragma unroll
-    for (int s = 0; s < C / 2; ++s) {  // 32 C slots of 16 codes: C / 2 per lane
-      const int slot = s * kWave + lane;
-      const u32x4 cw = *(const u32x4*)(smem + cbuf + slot * 16);
-      const uint32_t ww[4] = {cw.x, cw.y, cw.z, cw.w};
-      int idx[kSlot];
+      for (int j = 0; j < C; ++j) out[j * kWave + lane] = *(const uint4*)(smem + cbuf + (j * kWave + lane) * 16);
+    } else {
+      uint8_t* const out = a.idx_out + (size_t)row * ((size_t)kD * BITS / 8);
 #pragma unroll
-      for (int i = 0; i < kSlot; ++i) idx[i] = (int)((ww[i >> 2] >> (8 * (i & 3))) & 0xffu);
-      store_indices<BITS>(out, slot, idx);
+      for (int s = 0; s < C / 2; ++s) {  // 32 C slots of 16 codes: C / 2 per lane
+        const int slot = s * kWave + lane;
+        const u32x4 cw = *(const u32x4*)(smem + cbuf + slot * 16);
+        const uint32_t ww[4] = {cw.x, cw.y, cw.z, cw.w};
+        int idx[kSlot];
+#pragma unroll
+        for (int i = 0; i < kSlot; ++i) idx[i] = (int)((ww[i >> 2] >> (8 * (i & 3))) & 0xffu);
+        store_indices<BITS>(out, slot, idx);
+      }
     }
     wave_lds_sync();  // every lane has read its gathers and codes before the next row lands
   }
 }
 
-// LDS bytes per wave: the bf16 row and its code bytes.
-template <int C>
-constexpr int mfma_wave_bytes() { return 3 * 512 * C; }
+// LDS bytes per wave: the bf16 row and its code bytes (fp16 x' for the
+// rotation).
+template <int MODE, int C>
+constexpr int mfma_wave_bytes() { return (MODE == kRotF16 ? 4 : 3) * 512 * C; }
 
 template <int MODE, int BITS, int G, int C, bool kX>
 hipError_t launch_mfma_typed(RowArgs a, hipStream_t stream) {
   DeviceInfo di;
   hipError_t e = device_info(&di);
   if (e != hipSuccess) return e;
-  a.wave_bytes = mfma_wave_bytes<C>();
+  a.wave_bytes = mfma_wave_bytes<MODE, C>();
   int waves = 4;
   while (waves > 1 && a.grid_bytes + waves * a.wave_bytes > di.max_lds) waves >>= 1;
   const int lds = a.grid_bytes + waves * a.wave_bytes;
@@ -272,6 +289,19 @@ namespace rows {
       case 8: return launch_mfma_h<MODE, 8, G>(a, s);                          \
     }                                                                          \
     return hipErrorInvalidValue;                                               \
+  }
+
+}  // namespace rows
+}  // namespace orbit
+
+namespace orbit {
+namespace rows {
+
+// The fp16 rotation (no code width).
+#define ORBIT_ROWS_MFMA_ROT(G)                                                     \
+  template <>                                                                    \
+  hipError_t launch_mfma<kRotF16, G>(const RowArgs& a, int, hipStream_t s) {     \
+    return launch_mfma_d<kRotF16, 4, G, false>(a, s);                            \
   }
 
 }  // namespace rows

@@ -80,6 +80,14 @@ hipError_t launch_rows(const RowJob& job, hipStream_t stream) {
     if (e != hipSuccess) return e;
     mfma = job.rows > 16LL * di.n_cu;
   }
+  // the fp16 rotation of such rows, likewise
+  const bool mfma_rot = fast && job.mode == RowMode::kRotate && job.out_dtype == ORBIT_F16 &&
+                        job.d % 1024 == 0 && job.d <= 4096;
+  if (mfma_rot) {
+    if (job.h == 64) return launch_mfma<kRotF16, 2>(a, 0, stream);
+    if (job.h == 128) return launch_mfma<kRotF16, 4>(a, 0, stream);
+    return launch_mfma<kRotF16, 8>(a, 0, stream);
+  }
   if (mfma) {
     const bool act = job.mode == RowMode::kActQuant;
     if (job.h == 64) return act ? launch_mfma<kAct, 2>(a, job.bits, stream) : launch_mfma<kWeight, 2>(a, job.bits, stream);
