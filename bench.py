@@ -380,7 +380,11 @@ def main():
     # Per-kernel launch duration for the rooflines: the same kernels launched
     # back to back on the same stream, events around the whole run, so the
     # figure is the kernel's own duration (what a kernel trace reports)
-    # rather than the kernel plus the event gaps of the step loop.
+    # rather than the kernel plus the event overhead of the step loop.  Back
+    # to back, the GEMM finds its codes in L2 from its previous launch; in the
+    # steps the quantizer's stream has evicted them and a kernel trace shows
+    # it ~4 % slower there (the step_*_us fields carry the event-split step
+    # figures, which include the events' own overhead).
     def per_launch(fn, n):
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
