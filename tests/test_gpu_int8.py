@@ -44,6 +44,38 @@ def test_rotate_f16_and_f32(gpu_lib):
     assert diff.mean() < 1e-4
 
 
+def _check_f16_rotation(x16, ref):
+    ref16 = oracle.f16_bits_to_f64(oracle.f64_to_f16_bits(ref))
+    diff = x16 != ref16
+    if diff.any():  # only at fp16 rounding ties, as above
+        scale = np.abs(ref).max(axis=1, keepdims=True) * np.ones_like(ref)
+        ulp = np.spacing(np.abs(ref16[diff]).astype(np.float16)).astype(np.float64)
+        dist_to_tie = np.abs(np.abs(ref[diff] - ref16[diff]) - ulp / 2)
+        assert np.all(dist_to_tie <= 1e-6 * scale[diff])
+        assert np.all(np.abs(x16[diff] - ref16[diff]) <= ulp * 1.0001)
+    assert diff.mean() < 1e-4
+
+
+# fp16 rotations of bf16 rows with h = 64, 128, 256 and d = 1024 .. 4096 run
+# the Hadamard on the matrix cores; 93 rows, one of them zero
+@pytest.mark.parametrize("d,h,ident", [(1024, 64, False), (2048, 256, False), (3072, 128, False),
+                                        (4096, 64, False), (3072, 256, False), (2048, 128, True)])
+def test_rotate_f16_matrix_core_shapes(gpu_lib, d, h, ident):
+    # ident: Block-RHT (pi = identity)
+    rbp = gpu_lib
+    perm, signs = synth.rotation_params(d, 3 * d + h)
+    if ident:
+        perm = np.arange(d, dtype=np.int32)
+    g = np.random.default_rng(d - h)
+    X = synth.f32_to_bf16_bits(g.standard_normal((93, d)).astype(np.float32))
+    X[40] = 0
+    rot = rbp.Rotation(perm, signs, h)
+    ref = oracle.rpbh_rotate(as_f64(X), perm, signs, h)
+    x16 = oracle.f16_bits_to_f64(bits_of(rbp.rotate(rot, to_dev(X), torch.float16)))
+    assert np.all(x16[40] == 0)
+    _check_f16_rotation(x16, ref)
+
+
 def test_int8_pack_matches_oracle(gpu_lib):
     rbp = gpu_lib
     inp, rot = _setup(rbp, N=300)
