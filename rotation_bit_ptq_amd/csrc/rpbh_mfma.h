@@ -59,8 +59,160 @@ __device__ __forceinline__ void group_stages(float& v0, float& v1, float& v2, fl
   }
 }
 
-// kX: also write the debug copy of x' (activation mode; a separate
-// instantiation, so the plain kernel carries none of its registers).
+// The H_32 column halves as MFMA B operands: lane holds k = 8 kq + j of
+// column r16 (first half) and r16 + 16 (second half).
+__device__ __forceinline__ void hadamard32_operands(int r16, int kq, bf16x8& hb0, bf16x8& hb1) {
+  uint32_t hw0[4], hw1[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int k0 = 8 * kq + 2 * q;
+    hw0[q] = hadamard_bf16(k0, r16) | ((uint32_t)hadamard_bf16(k0 + 1, r16) << 16);
+    hw1[q] = hadamard_bf16(k0, r16 + 16) | ((uint32_t)hadamard_bf16(k0 + 1, r16 + 16) << 16);
+  }
+  hb0 = __builtin_bit_cast(bf16x8, make_uint4(hw0[0], hw0[1], hw0[2], hw0[3]));
+  hb1 = __builtin_bit_cast(bf16x8, make_uint4(hw1[0], hw1[1], hw1[2], hw1[3]));
+}
+
+// Gather offsets and sign masks of pairs c0 .. c0 + NP - 1.  Pair c covers
+// positions 512 c .. + 511 (16 / G whole blocks), group rho = 16 c +
+// (position % 512) / 32 being A row rho % 16; element j of the lane's
+// fragment is permuted position k = 512 c + 32 r16 + 8 kq + j, for any G.
+// y_k = D_k x[pi(k)] is the bf16 at byte 2 pi(k) of the row buffer with its
+// sign bit flipped when D_k < 0.  Elements 2 q and 2 q + 1 share offset
+// word q (16-bit byte offsets, low and high half) and mask word q.
+template <int NP>
+__device__ __forceinline__ void pair_offsets(const RowArgs& a, int c0, int r16, int kq,
+                                             uint32_t (&off)[NP][4], uint32_t (&sgn)[NP][4]) {
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int k0 = 512 * (c0 + i) + 32 * r16 + 8 * kq;
+    const i32x4 p0 = *(const i32x4*)(a.perm + k0), p1 = *(const i32x4*)(a.perm + k0 + 4);
+    const uint32_t sw = a.sign_bits[k0 >> 5] >> (k0 & 31);  // 8 signs (k0 % 8 == 0)
+    const int p[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      off[i][q] = ((uint32_t)p[2 * q] * 2u) | ((uint32_t)p[2 * q + 1] << 17);
+      sgn[i][q] = (((sw >> (2 * q)) & 1u) << 15) | (((sw >> (2 * q + 1)) & 1u) << 31);
+    }
+  }
+}
+
+// Pairs c0 .. c0 + NP - 1 of one row in the buffer at rbuf: gather, H_32 on
+// the matrix cores, H_G, then the codes (a byte per position at cbuf) or,
+// for kRotF16, fp16 x' (two bytes per position at cbuf); kX also writes
+// fp32 x' to xr.  The gathers of pair i + 1 and the grid-cell reads of
+// pair i are in flight while pair i is multiplied.
+template <int MODE, int G, int NP, bool kX>
+__device__ __forceinline__ void mfma_pairs(const RowArgs& a, uint32_t rbuf, uint32_t cbuf,
+                                           int c0, uint32_t (&off)[NP][4], const uint32_t (&sgn)[NP][4],
+                                           const bf16x8& hb0, const bf16x8& hb1, float alpha,
+                                           float* xr, int lane) {
+  // the kernel's dynamic LDS: with the array's known alignment the 8-byte
+  // grid cells are read as one ds_read_b64 rather than two 4-byte reads
+  extern __shared__ __align__(16) char smem[];
+  constexpr bool kQuant = MODE != kRotF16;
+  const int r16 = lane & 15, kq = lane >> 4;
+  const float top = kMagic + (float)(a.cells - 1);
+  const floatx4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  // (the empty asm keeps the offsets packed: unpacked once outside the row
+  // loop they would take twice the registers)
+  auto gather = [&](int i, uint32_t (&lo)[4], uint32_t (&hi)[4]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      asm volatile("" : "+v"(off[i][q]));
+      lo[q] = lds_read_u16(rbuf + (off[i][q] & 0xffffu));
+      hi[q] = lds_read_u16(rbuf + (off[i][q] >> 16));
+    }
+  };
+  uint32_t lo[4], hi[4];
+  gather(0, lo, hi);
+  float u[8];
+  GridCell g[8];
+#pragma unroll
+  for (int i = 0; i <= NP; ++i) {
+    float v[8];
+    if (i < NP) {
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) w[q] = (lo[q] | (hi[q] << 16)) ^ sgn[i][q];
+      const bf16x8 av = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+      if (i + 1 < NP) gather(i + 1, lo, hi);
+      const floatx4 y0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb0, zero, 0, 0, 0);
+      const floatx4 y1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb1, zero, 0, 0, 0);
+      // y0[e], y1[e]: A row 4 kq + e at columns r16 and r16 + 16, i.e.
+      // positions 512 c + 128 kq + 32 e + r16 (+ 16)
+      v[0] = y0[0]; v[1] = y0[1]; v[2] = y0[2]; v[3] = y0[3];
+      v[4] = y1[0]; v[5] = y1[1]; v[6] = y1[2]; v[7] = y1[3];
+    }
+    if (kQuant && i > 0) {  // the codes of pair i - 1
+      const int base = 512 * (c0 + i - 1) + 128 * kq + r16;  // position of element 0
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        smem[cbuf + base + 32 * (e & 3) + 16 * (e >> 2)] = (char)(g[e].base + (g[e].t < u[e] ? 1 : 0));
+    }
+    if (i < NP) {
+      group_stages<G>(v[0], v[1], v[2], v[3]);
+      group_stages<G>(v[4], v[5], v[6], v[7]);
+      if constexpr (G == 8) {  // groups t and t ^ 4 sit in lanes l and l ^ 16
+#pragma clang fp contract(off)
+        const float sg = (lane & 16) ? -1.0f : 1.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = xor_partner<16>(v[e]) + v[e] * sg;
+      }
+      const int base = 512 * (c0 + i) + 128 * kq + r16;
+      if constexpr (!kQuant) {  // fp16 x' into the staging buffer
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          *(uint16_t*)(smem + cbuf + 2 * (base + 32 * (e & 3) + 16 * (e >> 2))) = f32_to_f16_rne(v[e] * a.inv_sqrt_h);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          u[e] = v[e] * alpha;
+          g[e] = *(const GridCell*)(smem + grid_addr(u[e], a.ga, a.gb, top, a.grid_bias));
+        }
+        if constexpr (kX) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xr[base + 32 * (e & 3) + 16 * (e >> 2)] = v[e] * a.inv_sqrt_h;
+        }
+      }
+    }
+    // one pair at a time: hoisting later gathers would hold their registers
+    // and cost occupancy
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// The row's staged output: 16-code words for the codebook modes, 16-byte
+// pieces of fp16 x' for kRotF16; threads t0, t0 + NT, ... of the row's team
+// (a fixed trip count, so the loop unrolls and the code words keep their
+// own aligned stores).
+template <int MODE, int BITS, int D, int NT>
+__device__ __forceinline__ void store_row(const RowArgs& a, const char* smem, uint32_t cbuf,
+                                          long long row, int t0) {
+  if constexpr (MODE == kRotF16) {
+    static_assert((D / 8) % NT == 0, "whole rounds of 16-byte pieces");
+    uint4* const out = (uint4*)(a.xrot_f16 + (size_t)row * D);
+#pragma unroll
+    for (int s = 0; s < D / 8 / NT; ++s) out[s * NT + t0] = *(const uint4*)(smem + cbuf + (s * NT + t0) * 16);
+  } else {
+    static_assert((D / kSlot) % NT == 0, "whole rounds of code words");
+    uint8_t* const out = a.idx_out + (size_t)row * ((size_t)D * BITS / 8);
+#pragma unroll
+    for (int s = 0; s < D / kSlot / NT; ++s) {
+      const int slot = s * NT + t0;
+      const u32x4 cw = *(const u32x4*)(smem + cbuf + slot * 16);
+      const uint32_t ww[4] = {cw.x, cw.y, cw.z, cw.w};
+      int idx[kSlot];
+#pragma unroll
+      for (int i = 0; i < kSlot; ++i) idx[i] = (int)((ww[i >> 2] >> (8 * (i & 3))) & 0xffu);
+      store_indices<BITS>(out, slot, idx);
+    }
+  }
+}
+
+// Rows of 512 C coordinates, one wave per row.  kX: also write the debug
+// copy of x' (activation mode; a separate instantiation, so the plain kernel
+// carries none of its registers).
 template <int MODE, int BITS, int G, int C, bool kX>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C <= 6 ? 3 : 2))) void mfma_rows_kernel(RowArgs a) {
   static_assert(MODE == kAct || MODE == kWeight || MODE == kRotF16, "codebook modes and fp16 x'");
@@ -78,48 +230,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C <= 6 ? 3 
   const long long stride = (long long)gridDim.x * waves;
   long long row = (long long)blockIdx.x * waves + wave;
 
-  // B operands: the two column halves of H_32; lane holds k = 8 kq + j of
-  // column r16 (first half) and r16 + 16 (second half)
-  uint32_t hw0[4], hw1[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int k0 = 8 * kq + 2 * q;
-    hw0[q] = hadamard_bf16(k0, r16) | ((uint32_t)hadamard_bf16(k0 + 1, r16) << 16);
-    hw1[q] = hadamard_bf16(k0, r16 + 16) | ((uint32_t)hadamard_bf16(k0 + 1, r16 + 16) << 16);
-  }
-  const bf16x8 hb0 = __builtin_bit_cast(bf16x8, make_uint4(hw0[0], hw0[1], hw0[2], hw0[3]));
-  const bf16x8 hb1 = __builtin_bit_cast(bf16x8, make_uint4(hw1[0], hw1[1], hw1[2], hw1[3]));
-
-  // the first row's loads go out first; the loads of pi and the signs below
+  bf16x8 hb0, hb1;
+  hadamard32_operands(r16, kq, hb0, hb1);
+  // the first row's loads go out first; the loads of pi and the signs
   // overlap them
   RowRegs<uint16_t, C> pre;
   if (row < a.rows) pre.load(a, row, lane);
-
-  // gather offsets and sign masks.  Pair c covers positions 512 c .. + 511
-  // (16 / G whole blocks), group rho = 16 c + (position % 512) / 32 being A
-  // row rho % 16; element j of the lane's fragment is permuted position
-  // k = 512 c + 32 r16 + 8 kq + j, for any G; y_k = D_k x[pi(k)]
-  // is the bf16 at wbuf + 2 pi(k) with its sign bit flipped when D_k < 0.
-  // Elements 2 q and 2 q + 1 share offset word q (16-bit byte offsets,
-  // low and high half) and mask word q.
   uint32_t off[C][4], sgn[C][4];
-#pragma unroll
-  for (int c = 0; c < C; ++c) {
-    const int k0 = 512 * c + 32 * r16 + 8 * kq;
-    const i32x4 p0 = *(const i32x4*)(a.perm + k0), p1 = *(const i32x4*)(a.perm + k0 + 4);
-    const uint32_t sw = a.sign_bits[k0 >> 5] >> (k0 & 31);  // 8 signs (k0 % 8 == 0)
-    const int p[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      off[c][q] = ((uint32_t)p[2 * q] * 2u) | ((uint32_t)p[2 * q + 1] << 17);
-      sgn[c][q] = (((sw >> (2 * q)) & 1u) << 15) | (((sw >> (2 * q + 1)) & 1u) << 31);
-    }
-  }
-
+  pair_offsets<C>(a, 0, r16, kq, off, sgn);
   if constexpr (kQuant) build_grid(a, smem);
   __syncthreads();
-  const float top = kMagic + (float)(a.cells - 1);
-  const floatx4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
 
   for (; row < a.rows; row += stride) {
     float ssx = 0.0f;
@@ -130,97 +250,61 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C <= 6 ? 3 
     float alpha = 0.0f;
     if constexpr (kQuant) alpha = row_alpha<MODE, true>(a, wave_sum(ssx), row, lane);
     wave_lds_sync();
-    // the 8 bf16 of pair c's A fragment, read into the low halves of lo and
-    // hi (the empty asm keeps the offsets packed: unpacked once outside the
-    // row loop they would take twice the registers)
-    auto gather = [&](int c, uint32_t (&lo)[4], uint32_t (&hi)[4]) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        asm volatile("" : "+v"(off[c][q]));
-        lo[q] = lds_read_u16(wbuf + (off[c][q] & 0xffffu));
-        hi[q] = lds_read_u16(wbuf + (off[c][q] >> 16));
-      }
-    };
-    float* const xr = kX ? a.xrot_f32 + row * kD : nullptr;
-    uint32_t lo[4], hi[4];
-    gather(0, lo, hi);
-    // pair c's grid cells are read at its end and used at the next pair's
-    // start, so their LDS latency hides behind that pair's gather and MFMAs
-    float u[8];
-    GridCell g[8];
-#pragma unroll
-    for (int c = 0; c <= C; ++c) {
-      float v[8];
-      if (c < C) {
-        // pair c + 1 is gathered while pair c is multiplied
-        uint32_t w[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) w[q] = (lo[q] | (hi[q] << 16)) ^ sgn[c][q];
-        const bf16x8 av = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
-        if (c + 1 < C) gather(c + 1, lo, hi);
-        const floatx4 y0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb0, zero, 0, 0, 0);
-        const floatx4 y1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb1, zero, 0, 0, 0);
-        // y0[i], y1[i]: A row 4 kq + i at columns r16 and r16 + 16, i.e.
-        // positions 512 c + 128 kq + 32 i + r16 (+ 16)
-        v[0] = y0[0]; v[1] = y0[1]; v[2] = y0[2]; v[3] = y0[3];
-        v[4] = y1[0]; v[5] = y1[1]; v[6] = y1[2]; v[7] = y1[3];
-      }
-      if (kQuant && c > 0) {  // the codes of pair c - 1
-        const int base = 512 * (c - 1) + 128 * kq + r16;  // position of element 0
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          smem[cbuf + base + 32 * (e & 3) + 16 * (e >> 2)] = (char)(g[e].base + (g[e].t < u[e] ? 1 : 0));
-      }
-      if (c < C) {
-        group_stages<G>(v[0], v[1], v[2], v[3]);
-        group_stages<G>(v[4], v[5], v[6], v[7]);
-        if constexpr (G == 8) {  // groups t and t ^ 4 sit in lanes l and l ^ 16
-#pragma clang fp contract(off)
-          const float sg = (lane & 16) ? -1.0f : 1.0f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = xor_partner<16>(v[e]) + v[e] * sg;
-        }
-        if constexpr (!kQuant) {  // fp16 x' into the staging buffer
-          const int base = 512 * c + 128 * kq + r16;
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            *(uint16_t*)(smem + cbuf + 2 * (base + 32 * (e & 3) + 16 * (e >> 2))) = f32_to_f16_rne(v[e] * a.inv_sqrt_h);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            u[e] = v[e] * alpha;
-            g[e] = *(const GridCell*)(smem + grid_addr(u[e], a.ga, a.gb, top, a.grid_bias));
-          }
-          if constexpr (kX) {
-            const int base = 512 * c + 128 * kq + r16;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) xr[base + 32 * (e & 3) + 16 * (e >> 2)] = v[e] * a.inv_sqrt_h;
-          }
-        }
-      }
-      // one pair at a time: hoisting later gathers would hold their
-      // registers and cost occupancy
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    mfma_pairs<MODE, G, C, kX>(a, wbuf, cbuf, 0, off, sgn, hb0, hb1, alpha,
+                               kX ? a.xrot_f32 + row * kD : nullptr, lane);
     wave_lds_sync();  // the row's codes (or fp16 x') are in the staging buffer
-    if constexpr (!kQuant) {  // 64 C pieces of 16 bytes: C per lane
-      uint4* const out = (uint4*)(a.xrot_f16 + (size_t)row * kD);
-#pragma unroll
-      for (int j = 0; j < C; ++j) out[j * kWave + lane] = *(const uint4*)(smem + cbuf + (j * kWave + lane) * 16);
-    } else {
-      uint8_t* const out = a.idx_out + (size_t)row * ((size_t)kD * BITS / 8);
-#pragma unroll
-      for (int s = 0; s < C / 2; ++s) {  // 32 C slots of 16 codes: C / 2 per lane
-        const int slot = s * kWave + lane;
-        const u32x4 cw = *(const u32x4*)(smem + cbuf + slot * 16);
-        const uint32_t ww[4] = {cw.x, cw.y, cw.z, cw.w};
-        int idx[kSlot];
-#pragma unroll
-        for (int i = 0; i < kSlot; ++i) idx[i] = (int)((ww[i >> 2] >> (8 * (i & 3))) & 0xffu);
-        store_indices<BITS>(out, slot, idx);
-      }
-    }
+    store_row<MODE, BITS, kD, kWave>(a, smem, cbuf, row, lane);
     wave_lds_sync();  // every lane has read its gathers and codes before the next row lands
+  }
+}
+
+// Rows of 2048 CW coordinates (4096 < d <= 16384), one 4-wave workgroup per
+// row: wave w takes pairs CW w .. CW w + CW - 1, the squared norm comes from
+// a fixed-order workgroup reduction of the loaded row.
+template <int MODE, int BITS, int G, int CW, bool kX>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void mfma_long_kernel(RowArgs a) {
+  static_assert(MODE == kAct || MODE == kWeight, "codebook modes");
+  static_assert(G == 2 || G == 4 || G == 8, "h = 64, 128 or 256");
+  extern __shared__ __align__(16) char smem[];
+  constexpr int kD = 2048 * CW;
+  const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
+  float* const red = (float*)(smem + a.grid_bytes);        // four wave sums
+  const uint32_t rbuf = (uint32_t)a.grid_bytes + 16u;       // the row
+  const uint32_t cbuf = rbuf + 2u * kD;                     // one code byte per position
+  const int r16 = lane & 15, kq = lane >> 4;
+
+  bf16x8 hb0, hb1;
+  hadamard32_operands(r16, kq, hb0, hb1);
+  // thread t loads 16-byte chunks t + 256 i of the row
+  u32x4 pre[CW];
+  auto load = [&](long long rr) {
+    const u32x4* src = (const u32x4*)((const char*)a.in + (size_t)rr * kD * 2);
+#pragma unroll
+    for (int i = 0; i < CW; ++i) pre[i] = __builtin_nontemporal_load(src + t + 256 * i);
+  };
+  long long row = blockIdx.x;
+  if (row < a.rows) load(row);
+  uint32_t off[CW][4], sgn[CW][4];
+  pair_offsets<CW>(a, CW * wave, r16, kq, off, sgn);
+  build_grid(a, smem);
+
+  for (; row < a.rows; row += gridDim.x) {
+    float ssx = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CW; ++i) {
+      ssx = RowRegs<uint16_t, 1>::chunk_sumsq(pre[i], ssx);
+      *(u32x4*)(smem + rbuf + (t + 256 * i) * 16) = pre[i];
+    }
+    if (row + gridDim.x < a.rows) load(row + gridDim.x);
+    const float ws = wave_sum(ssx);
+    if (lane == 0) red[wave] = ws;
+    __syncthreads();  // the row, the wave sums (and, first time, the grid) are in LDS
+    const float alpha = row_alpha<MODE, true>(a, (red[0] + red[1]) + (red[2] + red[3]), row, t);
+    mfma_pairs<MODE, G, CW, kX>(a, rbuf, cbuf, CW * wave, off, sgn, hb0, hb1, alpha,
+                                kX ? a.xrot_f32 + row * kD : nullptr, lane);
+    __syncthreads();  // every wave's codes are in the byte buffer
+    store_row<MODE, BITS, kD, 256>(a, smem, cbuf, row, t);
+    __syncthreads();  // the buffers are free for the next row
   }
 }
 
@@ -251,6 +335,24 @@ hipError_t launch_mfma_typed(RowArgs a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int MODE, int BITS, int G, int CW, bool kX>
+hipError_t launch_mfma_long_typed(const RowArgs& a, hipStream_t stream) {
+  DeviceInfo di;
+  hipError_t e = device_info(&di);
+  if (e != hipSuccess) return e;
+  const int lds = a.grid_bytes + 16 + 3 * 2048 * CW;
+  if (lds > di.max_lds) return hipErrorInvalidValue;
+  auto kern = mfma_long_kernel<MODE, BITS, G, CW, kX>;
+  static LaunchCache cache;
+  int per_cu = 1;
+  e = prepare_launch(cache, (const void*)kern, 256, lds, &per_cu);
+  if (e != hipSuccess) return e;
+  const long long cap = (long long)di.n_cu * per_cu;
+  const int blocks = (int)(a.rows < cap ? a.rows : cap);
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), lds, stream, a);
+  return hipGetLastError();
+}
+
 template <int MODE, int BITS, int G, bool kX>
 hipError_t launch_mfma_d(const RowArgs& a, hipStream_t stream) {
   switch (a.d) {
@@ -258,6 +360,13 @@ hipError_t launch_mfma_d(const RowArgs& a, hipStream_t stream) {
     case 2048: return launch_mfma_typed<MODE, BITS, G, 4, kX>(a, stream);
     case 3072: return launch_mfma_typed<MODE, BITS, G, 6, kX>(a, stream);
     case 4096: return launch_mfma_typed<MODE, BITS, G, 8, kX>(a, stream);
+  }
+  if constexpr (MODE != kRotF16) {  // one workgroup per row
+    switch (a.d) {
+      case 8192: return launch_mfma_long_typed<MODE, BITS, G, 4, kX>(a, stream);
+      case 12288: return launch_mfma_long_typed<MODE, BITS, G, 6, kX>(a, stream);
+      case 16384: return launch_mfma_long_typed<MODE, BITS, G, 8, kX>(a, stream);
+    }
   }
   return hipErrorInvalidValue;
 }

@@ -68,12 +68,14 @@ hipError_t launch_rows(const RowJob& job, hipStream_t stream) {
   // the gather plan serves the kernels whose gather order it was built in
   // (transposed exactly when h allows it)
   if (job.gather && fast == tr_order) a.gather = job.gather;
-  // bf16 rows with h = 64, 128 or 256 and d = 1024, 2048, 3072 or 4096,
-  // codebook modes: the Hadamard runs on the matrix cores.  Measured on
-  // MI355X, the matrix-core kernel costs less per row but more to start a
-  // wave, and with 3072-wide rows (three waves per SIMD) it only wins once
-  // there are more than 16 rows per compute unit.
-  bool mfma = fast && quant && job.d % 1024 == 0 && job.d <= 4096;
+  // bf16 rows with h = 64, 128 or 256 and d = 1024, 2048, 3072, 4096 (one
+  // wave per row) or 8192, 12288, 16384 (one workgroup per row), codebook
+  // modes: the Hadamard runs on the matrix cores.  Measured on MI355X, the
+  // matrix-core kernel costs less per row but more to start a wave, and with
+  // 3072-wide rows (three waves per SIMD) it only wins once there are more
+  // than 16 rows per compute unit.
+  bool mfma = fast && quant &&
+              ((job.d % 1024 == 0 && job.d <= 4096) || job.d == 8192 || job.d == 12288 || job.d == 16384);
   if (mfma && job.d == 3072) {
     DeviceInfo di;
     const hipError_t e = device_info(&di);
