@@ -78,7 +78,14 @@ typedef struct {
    * row kernels read each lane's gather offsets directly instead of
    * deriving them from perm and sign_bits in every workgroup. */
   const uint16_t *gather;
+  /* ORBIT_RPBH_IDENTITY when perm[k] == k for every k (Block-RHT, or a
+   * permutation folded into the producer of the rows): a promise, not
+   * checked, that lets the matrix-core kernels read each fragment as
+   * contiguous bytes instead of gathering it.  0 otherwise. */
+  int32_t flags;
 } orbit_rpbh;
+
+#define ORBIT_RPBH_IDENTITY 1
 
 #define ORBIT_MAX_D 16384
 #define ORBIT_MAX_LEVELS 256

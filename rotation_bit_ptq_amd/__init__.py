@@ -50,7 +50,9 @@ class _Codebook(ctypes.Structure):
 class _RPBH(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("h", ctypes.c_int32),
                 ("perm", ctypes.c_void_p), ("sign_bits", ctypes.c_void_p),
-                ("gather", ctypes.c_void_p)]
+                ("gather", ctypes.c_void_p), ("flags", ctypes.c_int32)]
+
+RPBH_IDENTITY = 1  # perm is the identity (Block-RHT): rows are read without a gather
 
 
 def _load():
@@ -175,7 +177,9 @@ class Rotation:
         self.d, self.h = d, int(h)
         self.perm = torch.from_numpy(perm).to(device)
         self.sign_bits = torch.from_numpy(bits.view(np.int32)).to(device)
-        self.struct = _RPBH(d, int(h), self.perm.data_ptr(), self.sign_bits.data_ptr(), None)
+        ident = bool(np.array_equal(perm, np.arange(d, dtype=np.int32)))
+        self.struct = _RPBH(d, int(h), self.perm.data_ptr(), self.sign_bits.data_ptr(), None,
+                            RPBH_IDENTITY if ident else 0)
         self.gather = None
         n = lib.orbit_rpbh_gather_len(d, int(h)) if plan else 0
         if n > 0:

@@ -99,6 +99,7 @@ orbit_status group_pack(orbit::RowMode mode, const orbit_rpbh* rot, const void* 
   job.h = rot->h;
   job.perm = rot->perm;
   job.gather = rot->gather;
+  job.perm_identity = (rot->flags & ORBIT_RPBH_IDENTITY) != 0;
   job.sign_bits = rot->sign_bits;
   job.in = W;
   job.group = group;
@@ -244,6 +245,7 @@ orbit_status orbit_pack_weights(const orbit_rpbh* rot, const orbit_codebook* cw,
   job.h = rot->h;
   job.perm = rot->perm;
   job.gather = rot->gather;
+  job.perm_identity = (rot->flags & ORBIT_RPBH_IDENTITY) != 0;
   job.sign_bits = rot->sign_bits;
   job.in = W;
   job.bits = cw->bits;
@@ -272,6 +274,7 @@ orbit_status orbit_quant_act(const orbit_rpbh* rot, const orbit_codebook* ca, co
   job.h = rot->h;
   job.perm = rot->perm;
   job.gather = rot->gather;
+  job.perm_identity = (rot->flags & ORBIT_RPBH_IDENTITY) != 0;
   job.sign_bits = rot->sign_bits;
   job.in = X;
   job.bits = ca->bits;
@@ -299,6 +302,7 @@ orbit_status orbit_rotate(const orbit_rpbh* rot, const void* X, orbit_dtype x_dt
   job.h = rot->h;
   job.perm = rot->perm;
   job.gather = rot->gather;
+  job.perm_identity = (rot->flags & ORBIT_RPBH_IDENTITY) != 0;
   job.sign_bits = rot->sign_bits;
   job.in = X;
   if (out_dtype == ORBIT_F32) job.xrot_f32_out = (float*)out; else job.rot_out = out;

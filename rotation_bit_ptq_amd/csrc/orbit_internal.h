@@ -53,6 +53,7 @@ struct RowJob {
   const int32_t* perm;
   const uint32_t* sign_bits;
   const uint16_t* gather;  // the rotation's gather plan, or null
+  bool perm_identity;      // the caller's promise that perm[k] == k
   const void* in;
   // quantize outputs
   int bits;

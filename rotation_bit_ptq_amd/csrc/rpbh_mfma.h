@@ -80,15 +80,21 @@ __device__ __forceinline__ void hadamard32_operands(int r16, int kq, bf16x8& hb0
 // y_k = D_k x[pi(k)] is the bf16 at byte 2 pi(k) of the row buffer with its
 // sign bit flipped when D_k < 0.  Elements 2 q and 2 q + 1 share offset
 // word q (16-bit byte offsets, low and high half) and mask word q.
-template <int NP>
+// kIdent: pi is the identity (the caller's promise): no offsets are needed,
+// each fragment is 16 contiguous bytes of the row.
+template <int NP, bool kIdent>
 __device__ __forceinline__ void pair_offsets(const RowArgs& a, int c0, int r16, int kq,
                                              uint32_t (&off)[NP][4], uint32_t (&sgn)[NP][4]) {
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
     const int k0 = 512 * (c0 + i) + 32 * r16 + 8 * kq;
-    const i32x4 p0 = *(const i32x4*)(a.perm + k0), p1 = *(const i32x4*)(a.perm + k0 + 4);
     const uint32_t sw = a.sign_bits[k0 >> 5] >> (k0 & 31);  // 8 signs (k0 % 8 == 0)
-    const int p[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+    int p[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if constexpr (!kIdent) {
+      const i32x4 p0 = *(const i32x4*)(a.perm + k0), p1 = *(const i32x4*)(a.perm + k0 + 4);
+      p[0] = p0.x; p[1] = p0.y; p[2] = p0.z; p[3] = p0.w;
+      p[4] = p1.x; p[5] = p1.y; p[6] = p1.z; p[7] = p1.w;
+    }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       off[i][q] = ((uint32_t)p[2 * q] * 2u) | ((uint32_t)p[2 * q + 1] << 17);
@@ -102,7 +108,7 @@ __device__ __forceinline__ void pair_offsets(const RowArgs& a, int c0, int r16, 
 // for kRotF16, fp16 x' (two bytes per position at cbuf); kX also writes
 // fp32 x' to xr.  The gathers of pair i + 1 and the grid-cell reads of
 // pair i are in flight while pair i is multiplied.
-template <int MODE, int G, int NP, bool kX>
+template <int MODE, int G, int NP, bool kX, bool kIdent>
 __device__ __forceinline__ void mfma_pairs(const RowArgs& a, uint32_t rbuf, uint32_t cbuf,
                                            int c0, uint32_t (&off)[NP][4], const uint32_t (&sgn)[NP][4],
                                            const bf16x8& hb0, const bf16x8& hb1, float alpha,
@@ -117,6 +123,12 @@ __device__ __forceinline__ void mfma_pairs(const RowArgs& a, uint32_t rbuf, uint
   // (the empty asm keeps the offsets packed: unpacked once outside the row
   // loop they would take twice the registers)
   auto gather = [&](int i, uint32_t (&lo)[4], uint32_t (&hi)[4]) {
+    if constexpr (kIdent) {  // the fragment's 8 bf16 are contiguous: lo holds them in pairs
+      const u32x4 v = *(const u32x4*)(smem + rbuf + 2 * (512 * (c0 + i) + 32 * r16 + 8 * kq));
+      lo[0] = v.x; lo[1] = v.y; lo[2] = v.z; lo[3] = v.w;
+      hi[0] = hi[1] = hi[2] = hi[3] = 0u;
+      return;
+    }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       asm volatile("" : "+v"(off[i][q]));
@@ -213,7 +225,7 @@ __device__ __forceinline__ void store_row(const RowArgs& a, const char* smem, ui
 // Rows of 512 C coordinates, one wave per row.  kX: also write the debug
 // copy of x' (activation mode; a separate instantiation, so the plain kernel
 // carries none of its registers).
-template <int MODE, int BITS, int G, int C, bool kX>
+template <int MODE, int BITS, int G, int C, bool kX, bool kIdent>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C <= 6 ? 3 : 2))) void mfma_rows_kernel(RowArgs a) {
   static_assert(MODE == kAct || MODE == kWeight || MODE == kRotF16, "codebook modes and fp16 x'");
   constexpr bool kQuant = MODE != kRotF16;
@@ -237,7 +249,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C <= 6 ? 3 
   RowRegs<uint16_t, C> pre;
   if (row < a.rows) pre.load(a, row, lane);
   uint32_t off[C][4], sgn[C][4];
-  pair_offsets<C>(a, 0, r16, kq, off, sgn);
+  pair_offsets<C, kIdent>(a, 0, r16, kq, off, sgn);
   if constexpr (kQuant) build_grid(a, smem);
   __syncthreads();
 
@@ -250,7 +262,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C <= 6 ? 3 
     float alpha = 0.0f;
     if constexpr (kQuant) alpha = row_alpha<MODE, true>(a, wave_sum(ssx), row, lane);
     wave_lds_sync();
-    mfma_pairs<MODE, G, C, kX>(a, wbuf, cbuf, 0, off, sgn, hb0, hb1, alpha,
+    mfma_pairs<MODE, G, C, kX, kIdent>(a, wbuf, cbuf, 0, off, sgn, hb0, hb1, alpha,
                                kX ? a.xrot_f32 + row * kD : nullptr, lane);
     wave_lds_sync();  // the row's codes (or fp16 x') are in the staging buffer
     store_row<MODE, BITS, kD, kWave>(a, smem, cbuf, row, lane);
@@ -261,7 +273,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C <= 6 ? 3 
 // Rows of 2048 CW coordinates (4096 < d <= 16384), one 4-wave workgroup per
 // row: wave w takes pairs CW w .. CW w + CW - 1, the squared norm comes from
 // a fixed-order workgroup reduction of the loaded row.
-template <int MODE, int BITS, int G, int CW, bool kX>
+template <int MODE, int BITS, int G, int CW, bool kX, bool kIdent>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void mfma_long_kernel(RowArgs a) {
   static_assert(MODE == kAct || MODE == kWeight, "codebook modes");
   static_assert(G == 2 || G == 4 || G == 8, "h = 64, 128 or 256");
@@ -285,7 +297,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void m
   long long row = blockIdx.x;
   if (row < a.rows) load(row);
   uint32_t off[CW][4], sgn[CW][4];
-  pair_offsets<CW>(a, CW * wave, r16, kq, off, sgn);
+  pair_offsets<CW, kIdent>(a, CW * wave, r16, kq, off, sgn);
   build_grid(a, smem);
 
   for (; row < a.rows; row += gridDim.x) {
@@ -300,7 +312,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void m
     if (lane == 0) red[wave] = ws;
     __syncthreads();  // the row, the wave sums (and, first time, the grid) are in LDS
     const float alpha = row_alpha<MODE, true>(a, (red[0] + red[1]) + (red[2] + red[3]), row, t);
-    mfma_pairs<MODE, G, CW, kX>(a, rbuf, cbuf, CW * wave, off, sgn, hb0, hb1, alpha,
+    mfma_pairs<MODE, G, CW, kX, kIdent>(a, rbuf, cbuf, CW * wave, off, sgn, hb0, hb1, alpha,
                                 kX ? a.xrot_f32 + row * kD : nullptr, lane);
     __syncthreads();  // every wave's codes are in the byte buffer
     store_row<MODE, BITS, kD, 256>(a, smem, cbuf, row, t);
@@ -323,10 +335,11 @@ hipError_t launch_mfma_typed(RowArgs a, hipStream_t stream) {
   while (waves > 1 && a.grid_bytes + waves * a.wave_bytes > di.max_lds) waves >>= 1;
   const int lds = a.grid_bytes + waves * a.wave_bytes;
   if (lds > di.max_lds) return hipErrorInvalidValue;
-  auto kern = mfma_rows_kernel<MODE, BITS, G, C, kX>;
-  static LaunchCache cache;
+  auto kern = a.perm_identity ? mfma_rows_kernel<MODE, BITS, G, C, kX, true>
+                              : mfma_rows_kernel<MODE, BITS, G, C, kX, false>;
+  static LaunchCache cache, cache_ident;
   int per_cu = 1;
-  e = prepare_launch(cache, (const void*)kern, waves * kWave, lds, &per_cu);
+  e = prepare_launch(a.perm_identity ? cache_ident : cache, (const void*)kern, waves * kWave, lds, &per_cu);
   if (e != hipSuccess) return e;
   const long long need = (a.rows + waves - 1) / waves;
   const long long cap = (long long)di.n_cu * per_cu;
@@ -342,10 +355,11 @@ hipError_t launch_mfma_long_typed(const RowArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const int lds = a.grid_bytes + 16 + 3 * 2048 * CW;
   if (lds > di.max_lds) return hipErrorInvalidValue;
-  auto kern = mfma_long_kernel<MODE, BITS, G, CW, kX>;
-  static LaunchCache cache;
+  auto kern = a.perm_identity ? mfma_long_kernel<MODE, BITS, G, CW, kX, true>
+                              : mfma_long_kernel<MODE, BITS, G, CW, kX, false>;
+  static LaunchCache cache, cache_ident;
   int per_cu = 1;
-  e = prepare_launch(cache, (const void*)kern, 256, lds, &per_cu);
+  e = prepare_launch(a.perm_identity ? cache_ident : cache, (const void*)kern, 256, lds, &per_cu);
   if (e != hipSuccess) return e;
   const long long cap = (long long)di.n_cu * per_cu;
   const int blocks = (int)(a.rows < cap ? a.rows : cap);

@@ -20,6 +20,7 @@ hipError_t launch_rows(const RowJob& job, hipStream_t stream) {
   a.perm = job.perm;
   a.sign_bits = job.sign_bits;
   a.gather = nullptr;  // set below when the plan's order is the kernel's
+  a.perm_identity = job.perm_identity ? 1 : 0;
   a.in = job.in;
   a.sqrt_d_over_h = (float)sqrt((double)job.d / job.h);
   a.inv_sqrt_h = (float)(1.0 / sqrt((double)job.h));

@@ -96,6 +96,20 @@ def test_quant_act_matrix_core_shapes(gpu_lib, d, h, bits):
     _run_act(gpu_lib, X, perm, signs, h, bits, f"mfma-d{d}-h{h}-a{bits}")
 
 
+@pytest.mark.parametrize("d,h", [(2048, 128), (12288, 256), (1024, 64)])
+def test_quant_act_identity_permutation(gpu_lib, d, h):
+    # pi = identity (Block-RHT, or the MLP down layer with pi folded into the
+    # up layer): the binding flags it and the matrix-core kernels read each
+    # fragment as contiguous bytes instead of gathering it
+    _, signs = synth.rotation_params(d, 17 + d)
+    perm = np.arange(d, dtype=np.int32)
+    g = np.random.default_rng(h + d)
+    X = synth.f32_to_bf16_bits(g.standard_normal((70, d)).astype(np.float32))
+    rot = gpu_lib.Rotation(perm, signs, h)
+    assert rot.struct.flags == gpu_lib.RPBH_IDENTITY
+    _run_act(gpu_lib, X, perm, signs, h, 4, f"ident-d{d}-h{h}")
+
+
 def test_quant_act_matrix_core_3072_wide(gpu_lib):
     # 3072-wide rows take the matrix-core kernel above 16 rows per compute
     # unit (4096 on MI355X): 4100 rows, a ragged last round of waves
