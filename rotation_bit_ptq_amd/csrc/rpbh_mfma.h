@@ -73,18 +73,20 @@ __device__ __forceinline__ void hadamard32_operands(int r16, int kq, bf16x8& hb0
   hb1 = __builtin_bit_cast(bf16x8, make_uint4(hw1[0], hw1[1], hw1[2], hw1[3]));
 }
 
-// Gather offsets and sign masks of pairs c0 .. c0 + NP - 1.  Pair c covers
+// Gather offsets and signs of pairs c0 .. c0 + NP - 1.  Pair c covers
 // positions 512 c .. + 511 (16 / G whole blocks), group rho = 16 c +
 // (position % 512) / 32 being A row rho % 16; element j of the lane's
 // fragment is permuted position k = 512 c + 32 r16 + 8 kq + j, for any G.
 // y_k = D_k x[pi(k)] is the bf16 at byte 2 pi(k) of the row buffer with its
-// sign bit flipped when D_k < 0.  Elements 2 q and 2 q + 1 share offset
-// word q (16-bit byte offsets, low and high half) and mask word q.
-// kIdent: pi is the identity (the caller's promise): no offsets are needed,
-// each fragment is 16 contiguous bytes of the row.
+// sign bit flipped when D_k < 0.  Elements 2 q and 2 q + 1 share word q: the
+// low and high halves hold their byte offsets (below 2^15 for d <= 16384)
+// and, in bits 15 and 31, their sign flips, so the word masked with
+// 0x80008000 is the XOR that applies D to the gathered pair.
+// kIdent: pi is the identity (the caller's promise): the words hold only
+// the signs, and each fragment is 16 contiguous bytes of the row.
 template <int NP, bool kIdent>
 __device__ __forceinline__ void pair_offsets(const RowArgs& a, int c0, int r16, int kq,
-                                             uint32_t (&off)[NP][4], uint32_t (&sgn)[NP][4]) {
+                                             uint32_t (&off)[NP][4]) {
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
     const int k0 = 512 * (c0 + i) + 32 * r16 + 8 * kq;
@@ -96,10 +98,9 @@ __device__ __forceinline__ void pair_offsets(const RowArgs& a, int c0, int r16, 
       p[4] = p1.x; p[5] = p1.y; p[6] = p1.z; p[7] = p1.w;
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      off[i][q] = ((uint32_t)p[2 * q] * 2u) | ((uint32_t)p[2 * q + 1] << 17);
-      sgn[i][q] = (((sw >> (2 * q)) & 1u) << 15) | (((sw >> (2 * q + 1)) & 1u) << 31);
-    }
+    for (int q = 0; q < 4; ++q)
+      off[i][q] = ((uint32_t)p[2 * q] * 2u) | ((uint32_t)p[2 * q + 1] << 17) |
+                  (((sw >> (2 * q)) & 1u) << 15) | (((sw >> (2 * q + 1)) & 1u) << 31);
   }
 }
 
@@ -110,7 +111,7 @@ __device__ __forceinline__ void pair_offsets(const RowArgs& a, int c0, int r16, 
 // pair i are in flight while pair i is multiplied.
 template <int MODE, int G, int NP, bool kX, bool kIdent>
 __device__ __forceinline__ void mfma_pairs(const RowArgs& a, uint32_t rbuf, uint32_t cbuf,
-                                           int c0, uint32_t (&off)[NP][4], const uint32_t (&sgn)[NP][4],
+                                           int c0, uint32_t (&off)[NP][4],
                                            const bf16x8& hb0, const bf16x8& hb1, float alpha,
                                            float* xr, int lane) {
   // the kernel's dynamic LDS: with the array's known alignment the 8-byte
@@ -132,8 +133,8 @@ __device__ __forceinline__ void mfma_pairs(const RowArgs& a, uint32_t rbuf, uint
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       asm volatile("" : "+v"(off[i][q]));
-      lo[q] = lds_read_u16(rbuf + (off[i][q] & 0xffffu));
-      hi[q] = lds_read_u16(rbuf + (off[i][q] >> 16));
+      lo[q] = lds_read_u16(rbuf + (off[i][q] & 0x7fffu));
+      hi[q] = lds_read_u16(rbuf + ((off[i][q] >> 16) & 0x7fffu));
     }
   };
   uint32_t lo[4], hi[4];
@@ -146,7 +147,7 @@ __device__ __forceinline__ void mfma_pairs(const RowArgs& a, uint32_t rbuf, uint
     if (i < NP) {
       uint32_t w[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) w[q] = (lo[q] | (hi[q] << 16)) ^ sgn[i][q];
+      for (int q = 0; q < 4; ++q) w[q] = (lo[q] | (hi[q] << 16)) ^ (kIdent ? off[i][q] : off[i][q] & 0x80008000u);
       const bf16x8 av = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
       if (i + 1 < NP) gather(i + 1, lo, hi);
       const floatx4 y0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb0, zero, 0, 0, 0);
@@ -224,9 +225,14 @@ __device__ __forceinline__ void store_row(const RowArgs& a, const char* smem, ui
 
 // Rows of 512 C coordinates, one wave per row.  kX: also write the debug
 // copy of x' (activation mode; a separate instantiation, so the plain kernel
-// carries none of its registers).
+// carries none of its registers).  The occupancy hints are the register
+// budgets these instances meet without spills (hipcc's resource report):
+// four waves per SIMD up to 3072 coordinates except with 2-bit codes.
+constexpr int mfma_rows_waves(int bits, int c, bool x) {
+  return x ? (c <= 4 ? 3 : 2) : (c <= 6 && bits != 2 ? 4 : 3);
+}
 template <int MODE, int BITS, int G, int C, bool kX, bool kIdent>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C <= 6 ? 3 : 2))) void mfma_rows_kernel(RowArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(mfma_rows_waves(BITS, C, kX)))) void mfma_rows_kernel(RowArgs a) {
   static_assert(MODE == kAct || MODE == kWeight || MODE == kRotF16, "codebook modes and fp16 x'");
   constexpr bool kQuant = MODE != kRotF16;
   static_assert(C >= 1 && C <= 8, "rows of 512 C coordinates, C <= 8");
@@ -248,8 +254,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C <= 6 ? 3 
   // overlap them
   RowRegs<uint16_t, C> pre;
   if (row < a.rows) pre.load(a, row, lane);
-  uint32_t off[C][4], sgn[C][4];
-  pair_offsets<C, kIdent>(a, 0, r16, kq, off, sgn);
+  uint32_t off[C][4];
+  pair_offsets<C, kIdent>(a, 0, r16, kq, off);
   if constexpr (kQuant) build_grid(a, smem);
   __syncthreads();
 
@@ -262,7 +268,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C <= 6 ? 3 
     float alpha = 0.0f;
     if constexpr (kQuant) alpha = row_alpha<MODE, true>(a, wave_sum(ssx), row, lane);
     wave_lds_sync();
-    mfma_pairs<MODE, G, C, kX, kIdent>(a, wbuf, cbuf, 0, off, sgn, hb0, hb1, alpha,
+    mfma_pairs<MODE, G, C, kX, kIdent>(a, wbuf, cbuf, 0, off, hb0, hb1, alpha,
                                kX ? a.xrot_f32 + row * kD : nullptr, lane);
     wave_lds_sync();  // the row's codes (or fp16 x') are in the staging buffer
     store_row<MODE, BITS, kD, kWave>(a, smem, cbuf, row, lane);
@@ -274,7 +280,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C <= 6 ? 3 
 // row: wave w takes pairs CW w .. CW w + CW - 1, the squared norm comes from
 // a fixed-order workgroup reduction of the loaded row.
 template <int MODE, int BITS, int G, int CW, bool kX, bool kIdent>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void mfma_long_kernel(RowArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kX ? 2 : (CW <= 6 ? 4 : 3)))) void mfma_long_kernel(RowArgs a) {
   static_assert(MODE == kAct || MODE == kWeight, "codebook modes");
   static_assert(G == 2 || G == 4 || G == 8, "h = 64, 128 or 256");
   extern __shared__ __align__(16) char smem[];
@@ -296,8 +302,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void m
   };
   long long row = blockIdx.x;
   if (row < a.rows) load(row);
-  uint32_t off[CW][4], sgn[CW][4];
-  pair_offsets<CW, kIdent>(a, CW * wave, r16, kq, off, sgn);
+  uint32_t off[CW][4];
+  pair_offsets<CW, kIdent>(a, CW * wave, r16, kq, off);
   build_grid(a, smem);
 
   for (; row < a.rows; row += gridDim.x) {
@@ -312,7 +318,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void m
     if (lane == 0) red[wave] = ws;
     __syncthreads();  // the row, the wave sums (and, first time, the grid) are in LDS
     const float alpha = row_alpha<MODE, true>(a, (red[0] + red[1]) + (red[2] + red[3]), row, t);
-    mfma_pairs<MODE, G, CW, kX, kIdent>(a, rbuf, cbuf, CW * wave, off, sgn, hb0, hb1, alpha,
+    mfma_pairs<MODE, G, CW, kX, kIdent>(a, rbuf, cbuf, CW * wave, off, hb0, hb1, alpha,
                                 kX ? a.xrot_f32 + row * kD : nullptr, lane);
     __syncthreads();  // every wave's codes are in the byte buffer
     store_row<MODE, BITS, kD, 256>(a, smem, cbuf, row, t);
