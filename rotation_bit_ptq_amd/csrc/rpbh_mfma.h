@@ -250,13 +250,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(mfma_rows_w
 
   bf16x8 hb0, hb1;
   hadamard32_operands(r16, kq, hb0, hb1);
-  // the first row's loads go out first; the loads of pi and the signs
-  // overlap them
-  RowRegs<uint16_t, C> pre;
-  if (row < a.rows) pre.load(a, row, lane);
+  // Load order.  Global loads retire in order, so waits for the signs, pi
+  // and the grid issued behind the row's loads wait for the row as well.
+  // With pi = identity only the sign words precede the row (measured: 4096
+  // rows of 3072, 11.3 -> 10.5 us).  A random pi is 4 bytes per coordinate
+  // that every wave reads whole; issued by all waves at once ahead of the
+  // rows those reads contend in L2 (14.7 -> 18.9 us), so there the row goes
+  // first.  The row load is unconditional (a spare wave reads the last row)
+  // so that the compiler counts it on every path.
   uint32_t off[C][4];
-  pair_offsets<C, kIdent>(a, 0, r16, kq, off);
-  if constexpr (kQuant) build_grid(a, smem);
+  RowRegs<uint16_t, C> pre;
+  if constexpr (kIdent) {
+    pair_offsets<C, kIdent>(a, 0, r16, kq, off);
+    if constexpr (kQuant) build_grid(a, smem);
+    pre.load(a, row < a.rows ? row : a.rows - 1, lane);
+  } else {
+    pre.load(a, row < a.rows ? row : a.rows - 1, lane);
+    pair_offsets<C, kIdent>(a, 0, r16, kq, off);
+    if constexpr (kQuant) build_grid(a, smem);
+  }
   __syncthreads();
 
   for (; row < a.rows; row += stride) {
@@ -300,11 +312,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kX ? 2 : (C
 #pragma unroll
     for (int i = 0; i < CW; ++i) pre[i] = __builtin_nontemporal_load(src + t + 256 * i);
   };
+  // the load order of the row kernel (the launch gives every workgroup a
+  // row)
   long long row = blockIdx.x;
-  if (row < a.rows) load(row);
   uint32_t off[CW][4];
-  pair_offsets<CW, kIdent>(a, CW * wave, r16, kq, off);
-  build_grid(a, smem);
+  if constexpr (kIdent) {
+    pair_offsets<CW, kIdent>(a, CW * wave, r16, kq, off);
+    build_grid(a, smem);
+    load(row);
+  } else {
+    load(row);
+    pair_offsets<CW, kIdent>(a, CW * wave, r16, kq, off);
+    build_grid(a, smem);
+  }
 
   for (; row < a.rows; row += gridDim.x) {
     float ssx = 0.0f;
