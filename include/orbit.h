@@ -110,7 +110,9 @@ int orbit_last_hip_error(void);
 
 /* Length in uint16 entries of the gather plan of a rotation of dimension d
  * and block h: 1024 per round of 1024 coordinates, at least 4096
- * (1024 * max(4, ceil(d / 1024))); 0 for invalid d, h.  Host only. */
+ * (L = 1024 * max(4, ceil(d / 1024))), plus d entries of matrix-core words
+ * when h is 64, 128 or 256 and d is a multiple of 512 (d <= 16384); 0 for
+ * invalid d, h.  Host only. */
 int64_t orbit_rpbh_gather_len(int32_t d, int32_t h);
 
 /* Builds the gather plan of `rot` (its `gather` field is ignored) into the
@@ -123,6 +125,11 @@ int64_t orbit_rpbh_gather_len(int32_t d, int32_t h);
  * s = 64 r + l: k = 16 s + e in general; for h = 64, 128 and 256 (T = h/16
  * lanes per Hadamard block, G = 16/T, p = s mod T, e = G t + i) the order
  * that applies H_h = H_T x H_16 as H_T first: k = 16 (s - p) + 16 t + G p + i.
+ * The matrix-core section (when present) follows at entry L as uint32 words:
+ * word 4 (64 c + l) + q covers the permuted coordinates k and k + 1, k =
+ * 512 c + 32 (l mod 16) + 8 floor(l / 16) + 2 q, as 2 perm[k] | (D_k = -1) <<
+ * 15 | 2 perm[k + 1] << 16 | (D_{k+1} = -1) << 31 (byte offsets of the bf16
+ * coordinates in the row, and their sign flips).
  * Errors: ORBIT_E_ARG (null or misaligned pointers), ORBIT_E_SHAPE (d, h),
  * ORBIT_E_HIP. */
 orbit_status orbit_rpbh_build_gather(const orbit_rpbh *rot, uint16_t *out, hipStream_t stream);

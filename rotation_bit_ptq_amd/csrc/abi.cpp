@@ -215,7 +215,7 @@ int orbit_last_hip_error(void) { return g_last_hip_error; }
 int64_t orbit_rpbh_gather_len(int32_t d, int32_t h) {
   if (d < 16 || d > ORBIT_MAX_D || !pow2(h) || h < 16 || h > 4096 || d % h) return 0;
   if (h > 1024 && d > 4096) return 0;
-  return orbit::gather_len(d);
+  return (int64_t)orbit::gather_len(d) + orbit::mfma_words_len(d, h);
 }
 
 orbit_status orbit_rpbh_build_gather(const orbit_rpbh* rot, uint16_t* out, hipStream_t stream) {

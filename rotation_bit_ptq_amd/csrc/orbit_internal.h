@@ -79,6 +79,14 @@ __host__ __device__ inline int gather_len(int d) {
   const int rounds = (d + 1023) / 1024;
   return 1024 * (rounds < 4 ? 4 : rounds);
 }
+
+// The plan's second section, after gather_len(d) entries: the matrix-core
+// kernels' packed offset words (two uint16 entries per word, one word per
+// pair of coordinates), for the rotations those kernels can take (the
+// 15-bit byte offsets need d <= 16384).
+__host__ __device__ inline int mfma_words_len(int d, int h) {
+  return ((h == 64 || h == 128 || h == 256) && d % 512 == 0 && d <= 16384) ? d : 0;
+}
 hipError_t launch_gather_plan(int d, int h, const int32_t* perm, const uint32_t* sign_bits,
                               uint16_t* out, hipStream_t stream);
 

@@ -84,9 +84,20 @@ __device__ __forceinline__ void hadamard32_operands(int r16, int kq, bf16x8& hb0
 // 0x80008000 is the XOR that applies D to the gathered pair.
 // kIdent: pi is the identity (the caller's promise): the words hold only
 // the signs, and each fragment is 16 contiguous bytes of the row.
+// With the rotation's plan the words of a random pi are read from it
+// (16 bytes per lane and pair) instead of being built from pi and the signs.
 template <int NP, bool kIdent>
 __device__ __forceinline__ void pair_offsets(const RowArgs& a, int c0, int r16, int kq,
                                              uint32_t (&off)[NP][4]) {
+  if (!kIdent && a.mfma_words) {  // uniform
+    const int lane = 16 * kq + r16;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const u32x4 w = *(const u32x4*)(a.mfma_words + 4 * (64 * (c0 + i) + lane));
+      off[i][0] = w.x; off[i][1] = w.y; off[i][2] = w.z; off[i][3] = w.w;
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
     const int k0 = 512 * (c0 + i) + 32 * r16 + 8 * kq;

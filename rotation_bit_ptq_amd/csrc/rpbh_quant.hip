@@ -69,20 +69,18 @@ hipError_t launch_rows(const RowJob& job, hipStream_t stream) {
   // the gather plan serves the kernels whose gather order it was built in
   // (transposed exactly when h allows it)
   if (job.gather && fast == tr_order) a.gather = job.gather;
+  a.mfma_words = job.gather && mfma_words_len(job.d, job.h) > 0
+                     ? (const uint32_t*)(job.gather + gather_len(job.d)) : nullptr;
   // bf16 rows with h = 64, 128 or 256 and d = 1024, 2048, 3072, 4096 (one
   // wave per row) or 8192, 12288, 16384 (one workgroup per row), codebook
-  // modes: the Hadamard runs on the matrix cores.  Measured on MI355X, the
-  // matrix-core kernel costs less per row but more to start a wave, and with
-  // 3072-wide rows (three waves per SIMD) it only wins once there are more
-  // than 16 rows per compute unit.
-  bool mfma = fast && quant &&
-              ((job.d % 1024 == 0 && job.d <= 4096) || job.d == 8192 || job.d == 12288 || job.d == 16384);
-  if (mfma && job.d == 3072) {
-    DeviceInfo di;
-    const hipError_t e = device_info(&di);
-    if (e != hipSuccess) return e;
-    mfma = job.rows > 16LL * di.n_cu;
-  }
+  // modes: the Hadamard runs on the matrix cores.  Measured on MI355X, with
+  // the rotation's plan (offset words read, not built per wave) it beats the
+  // butterfly kernels at every size measured (4096 x 3072: 11.8 against
+  // 14.0 us); without the plan it is 4 % behind at 16 rows of 3072 per
+  // compute unit and ahead above that.  The choice does not depend on the
+  // plan, so results never do.
+  const bool mfma = fast && quant &&
+                    ((job.d % 1024 == 0 && job.d <= 4096) || job.d == 8192 || job.d == 12288 || job.d == 16384);
   // the fp16 rotation of such rows, likewise
   const bool mfma_rot = fast && job.mode == RowMode::kRotate && job.out_dtype == ORBIT_F16 &&
                         job.d % 1024 == 0 && job.d <= 4096;
@@ -170,8 +168,27 @@ __global__ __launch_bounds__(256) void gather_plan_kernel(int d, const int32_t* 
   out[i] = (uint16_t)v;
 }
 
+// The plan's matrix-core section: word 4 (64 c + l) + q serves lane l of
+// pair c (positions 512 c .. + 511), element pair 2 q, 2 q + 1 of the lane's
+// fragment, i.e. permuted coordinates k and k + 1 with k = 512 c + 32 (l %
+// 16) + 8 (l / 16) + 2 q: byte offsets 2 pi(k) and 2 pi(k + 1) in the low
+// and high halves, their sign flips in bits 15 and 31.
+__global__ __launch_bounds__(256) void mfma_words_kernel(int d, const int32_t* perm,
+                                                         const uint32_t* sign_bits, uint32_t* out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= d / 2) return;
+  const int c = i >> 8, l = (i >> 2) & 63, q = i & 3;
+  const int k = 512 * c + 32 * (l & 15) + 8 * (l >> 4) + 2 * q;
+  const uint32_t s0 = (sign_bits[k >> 5] >> (k & 31)) & 1u;
+  const uint32_t s1 = (sign_bits[(k + 1) >> 5] >> ((k + 1) & 31)) & 1u;
+  out[i] = ((uint32_t)perm[k] * 2u) | ((uint32_t)perm[k + 1] << 17) | (s0 << 15) | (s1 << 31);
+}
+
 hipError_t launch_gather_plan(int d, int h, const int32_t* perm, const uint32_t* sign_bits,
                               uint16_t* out, hipStream_t stream) {
+  if (mfma_words_len(d, h) > 0)
+    hipLaunchKernelGGL(mfma_words_kernel, dim3((d / 2 + 255) / 256), dim3(256), 0, stream, d, perm, sign_bits,
+                       (uint32_t*)(out + gather_len(d)));
   const dim3 grid(gather_len(d) / 256), block(256);
   if (h == 64) hipLaunchKernelGGL(gather_plan_kernel<2>, grid, block, 0, stream, d, perm, sign_bits, out);
   else if (h == 128) hipLaunchKernelGGL(gather_plan_kernel<3>, grid, block, 0, stream, d, perm, sign_bits, out);

@@ -38,13 +38,39 @@ def _plan_reference(perm, signs, h, rounds=4):
     return out
 
 
+def _words_reference(perm, signs, h):
+    """The documented matrix-core section: word 4 (64 c + l) + q covers
+    permuted coordinates k, k + 1 with k = 512 c + 32 (l % 16) + 8 (l // 16)
+    + 2 q; empty unless h is 64, 128 or 256 and d % 512 == 0."""
+    d = perm.shape[0]
+    if h not in (64, 128, 256) or d % 512:
+        return np.zeros(0, dtype=np.int64)
+    out = np.zeros(d // 2, dtype=np.int64)
+    for c in range(d // 512):
+        for lane in range(64):
+            for q in range(4):
+                k = 512 * c + 32 * (lane % 16) + 8 * (lane // 16) + 2 * q
+                out[4 * (64 * c + lane) + q] = (2 * int(perm[k]) | (int(signs[k] < 0) << 15)
+                                                | (2 * int(perm[k + 1])) << 16
+                                                | (int(signs[k + 1] < 0) << 31))
+    return out
+
+
+def _check_plan(rot, perm, signs, h, rounds):
+    got = rot.gather.cpu().numpy()
+    n = 1024 * rounds
+    words = _words_reference(perm, signs, h)
+    assert got.shape == (n + 2 * words.shape[0],)
+    assert np.array_equal(got[:n].view(np.uint16).astype(np.int64), _plan_reference(perm, signs, h, rounds))
+    assert np.array_equal(got[n:].view(np.uint32).astype(np.int64), words)
+
+
 @pytest.mark.parametrize("d,h", [(3072, 128), (1024, 64), (2048, 256), (512, 32), (96, 16)])
 def test_plan_layout(gpu_lib, d, h):
     perm, signs = synth.rotation_params(d, 7 + d + h)
     rot = gpu_lib.Rotation(perm, signs, h)
     torch.cuda.synchronize()
-    got = rot.gather.cpu().numpy().view(np.uint16).astype(np.int64)
-    assert np.array_equal(got, _plan_reference(perm, signs, h))
+    _check_plan(rot, perm, signs, h, 4)
 
 
 def test_plan_for_long_rows(gpu_lib):
@@ -52,15 +78,15 @@ def test_plan_for_long_rows(gpu_lib):
     perm, signs = synth.rotation_params(d, 3)
     rot = gpu_lib.Rotation(perm, signs, h)
     torch.cuda.synchronize()
-    got = rot.gather.cpu().numpy().view(np.uint16).astype(np.int64)
-    assert got.shape == (12288,)
-    assert np.array_equal(got, _plan_reference(perm, signs, h, rounds=12))
+    _check_plan(rot, perm, signs, h, 12)
 
 
 @pytest.mark.parametrize("cfg,K,h,bits,f32", [
     (2, 3072, 128, 4, False),   # transposed-gather kernel, bf16
-    (2, 1024, 64, 2, False),
+    (2, 1024, 64, 2, False),    # matrix-core kernel: words from the plan or from pi
     (2, 2048, 256, 6, False),
+    (2, 4096, 128, 3, False),
+    (2, 12288, 256, 4, False),  # matrix-core long-row kernel
     (2, 512, 32, 4, False),     # consecutive order, bf16
     (2, 3072, 128, 1, False),   # 1-bit codes: consecutive kernel, plan order differs -> unused
     (1, 256, 64, 4, True),      # fp32 rows: consecutive kernel, plan order differs -> unused
@@ -78,9 +104,13 @@ def test_quant_act_same_with_and_without_plan(gpu_lib, cfg, K, h, bits, f32):
     assert with_plan.gather is not None and without.gather is None
     i1, s1, x1 = rbp.quant_act(with_plan, cb, X, synth.EPS, debug_xrot=True)
     i2, s2, x2 = rbp.quant_act(without, cb, X, synth.EPS, debug_xrot=True)
+    # the production instances (no debug copy of x') as well
+    i3, s3 = rbp.quant_act(with_plan, cb, X, synth.EPS)
+    i4, s4 = rbp.quant_act(without, cb, X, synth.EPS)
     torch.cuda.synchronize()
-    assert torch.equal(i1, i2)
+    assert torch.equal(i1, i2) and torch.equal(i3, i4) and torch.equal(i1, i3)
     assert torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+    assert torch.equal(s3.view(torch.int32), s4.view(torch.int32))
     assert torch.equal(x1.view(torch.int32), x2.view(torch.int32))
 
 

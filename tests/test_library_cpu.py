@@ -156,3 +156,18 @@ def test_status_strings():
                        (3, b"unsupported dtype"), (4, b"unsupported configuration"),
                        (5, b"HIP error")]:
         assert lib.orbit_status_string(code) == text
+
+
+@pytest.mark.parametrize("d,h,expect", [
+    (3072, 128, 4096 + 3072),    # butterfly section (at least 4 rounds) + matrix-core words
+    (1024, 64, 4096 + 1024),
+    (12288, 256, 12288 + 12288),
+    (16384, 128, 16384 + 16384),
+    (512, 32, 4096),             # h = 32: no matrix-core kernel, no words
+    (96, 16, 4096),              # d not a multiple of 512
+    (2048, 512, 4096),
+    (3072, 100, 0),              # h not a power of two
+    (100, 64, 0),                # d not a multiple of h
+])
+def test_gather_plan_length(d, h, expect):
+    assert _lib().lib.orbit_rpbh_gather_len(d, h) == expect
