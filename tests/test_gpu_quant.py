@@ -74,8 +74,13 @@ def test_quant_act_long_rows(gpu_lib):
     _run_act(gpu_lib, X, inp["perm2"], inp["signs2"], 256, 4, "down-d12288")
 
 
+# (512, 64), (1536, 128), (2560, 256), (6144, 128): bf16 rows with h = 64,
+# 128, 256 whose width the matrix-core kernels do not take, so the
+# transposed-gather butterfly kernels (one wave per row, or one workgroup
+# per row past 4096) run them
 @pytest.mark.parametrize("d,h", [(1040, 16), (48, 16), (3072, 32), (3072, 1024), (1024, 1024),
-                                 (2048, 2048), (4096, 4096), (4096, 2048)])
+                                 (2048, 2048), (4096, 4096), (4096, 2048),
+                                 (512, 64), (1536, 128), (2560, 256), (6144, 128)])
 def test_quant_act_shapes(gpu_lib, d, h):
     perm, signs = synth.rotation_params(d, 100 + d + h)
     g = np.random.default_rng(d + h)
@@ -203,6 +208,29 @@ def test_weight_pack_workloads(gpu_lib):
             hi = oracle.bf16_bits_to_f64(oracle.f64_to_bf16_bits(r64 * (1 + 1e-6)))
             assert np.all(lo != hi), f"{label}: r mismatch off a tie"
         assert got_r[3] == 0
+
+
+@pytest.mark.parametrize("d,h", [(1536, 128), (512, 64)])
+def test_weight_pack_butterfly_widths(gpu_lib, d, h):
+    # bf16 weight rows whose width the matrix-core kernels do not take
+    rbp = gpu_lib
+    perm, signs = synth.rotation_params(d, 11 * d + h)
+    g = np.random.default_rng(5 * d + h)
+    W = synth.f32_to_bf16_bits(g.standard_normal((90, d)).astype(np.float32))
+    rot = rbp.Rotation(perm, signs, h)
+    cb = rbp.Codebook(d, 4)
+    ref_cb = oracle.codebook(4)
+    idx, r = rbp.pack_weights(rot, cb, to_dev(W))
+    torch.cuda.synchronize()
+    ref = oracle.pack_weights(as_f64(W), perm, signs, h, ref_cb, 4)
+    check_indices(idx, 4, d, ref["u"], ref_cb["thresholds"], f"w-d{d}-h{h}")
+    got_r = bits_of(r)
+    bad = got_r != ref["r_bf16"]
+    if bad.any():
+        r64 = ref["r"][bad]
+        lo = oracle.bf16_bits_to_f64(oracle.f64_to_bf16_bits(r64 * (1 - 1e-6)))
+        hi = oracle.bf16_bits_to_f64(oracle.f64_to_bf16_bits(r64 * (1 + 1e-6)))
+        assert np.all(lo != hi), "r mismatch off a tie"
 
 
 def test_weight_pack_long_rows(gpu_lib):
