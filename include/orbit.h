@@ -34,7 +34,7 @@
  *     the host before any HIP call; a bad argument returns ORBIT_E_ARG
  *     (null pointer, bad enum, unsorted codebook), ORBIT_E_SHAPE (sizes) or
  *     ORBIT_E_DTYPE, with nothing enqueued.  A failed launch returns
- *     ORBIT_E_HIP and orbit_last_hip_error() gives the HIP code.
+ *     ORBIT_E_HIP and orbit_last_hip_error reports the HIP code.
  */
 #ifndef ORBIT_H
 #define ORBIT_H
@@ -78,10 +78,13 @@ typedef struct {
    * row kernels read each lane's gather offsets directly instead of
    * deriving them from perm and sign_bits in every workgroup. */
   const uint16_t *gather;
-  /* ORBIT_RPBH_IDENTITY when perm[k] == k for every k (Block-RHT, or a
-   * permutation folded into the producer of the rows): a promise, not
-   * checked, that lets the matrix-core kernels read each fragment as
-   * contiguous bytes instead of gathering it.  0 otherwise. */
+  /* Set by orbit_rpbh_build_gather, not by the caller:
+   * ORBIT_RPBH_IDENTITY when it found perm[k] == k for every k (Block-RHT,
+   * or a permutation folded into the producer of the rows), which lets the
+   * matrix-core kernels read each fragment as contiguous bytes instead of
+   * gathering it; 0 otherwise.  The entry points honour the bit only
+   * together with a gather plan (gather != NULL); without one it is ignored
+   * and the rows are gathered through perm. */
   int32_t flags;
 } orbit_rpbh;
 
@@ -105,8 +108,10 @@ typedef struct {
 /* Text of a status code (static storage). */
 const char *orbit_status_string(orbit_status status);
 
-/* The last HIP error code seen by a failed call on this thread (0 if none). */
-int orbit_last_hip_error(void);
+/* Writes to *hip_error_out the HIP error code of the last call on this
+ * thread that returned ORBIT_E_HIP (0 if none has).  Host only.
+ * Errors: ORBIT_E_ARG (hip_error_out NULL). */
+orbit_status orbit_last_hip_error(int *hip_error_out);
 
 /* Length in uint16 entries of the gather plan of a rotation of dimension d
  * and block h: 1024 per round of 1024 coordinates, at least 4096
@@ -117,7 +122,9 @@ int64_t orbit_rpbh_gather_len(int32_t d, int32_t h);
 
 /* Builds the gather plan of `rot` (its `gather` field is ignored) into the
  * device buffer `out` of orbit_rpbh_gather_len(d, h) entries, 16-byte
- * aligned, asynchronously on `stream`.  Entry r*1024 + l*16 + e is the
+ * aligned, on `stream`, and sets rot->flags: it reads perm back to the host
+ * once (so the call synchronizes `stream`) and sets ORBIT_RPBH_IDENTITY
+ * exactly when perm is the identity.  Entry r*1024 + l*16 + e is the
  * offset, in elements of the row buffer that holds x followed by -x, of the
  * coordinate y_k = D_k x[perm[k]] (OrbitQuant page, Method: P_pi then the
  * signs) that lane l gathers as element e of round r, i.e.
@@ -132,7 +139,7 @@ int64_t orbit_rpbh_gather_len(int32_t d, int32_t h);
  * coordinates in the row, and their sign flips).
  * Errors: ORBIT_E_ARG (null or misaligned pointers), ORBIT_E_SHAPE (d, h),
  * ORBIT_E_HIP. */
-orbit_status orbit_rpbh_build_gather(const orbit_rpbh *rot, uint16_t *out, hipStream_t stream);
+orbit_status orbit_rpbh_build_gather(orbit_rpbh *rot, uint16_t *out, hipStream_t stream);
 
 /* Fit the Lloyd-Max codebook for N(0,1) with 2^bits levels, in fp64, on the
  * host (OrbitQuant page, Method: Lloyd-Max run offline on the marginal).
@@ -211,9 +218,15 @@ orbit_status orbit_qlinear_act(const uint8_t *idx_a, const float *s, const orbit
                                int64_t M, int64_t N, int64_t K, void *out, orbit_dtype out_dtype,
                                orbit_act act, hipStream_t stream);
 
-/* Rotation alone: out = Pi x per row (the int8 path's run-time step, and a
- * debugging aid).  X: device [M, d] F32 or BF16; out: device [M, d],
- * out_dtype F32 or F16 (nearest even). */
+/* Rotation alone: out = Pi x per row, the online rotation x' = Pi_d x of the
+ * OrbitQuant page, Method, without the norm split and the codebook.  It is
+ * the int8 article's load-and-run step (section 4) in the equal form that
+ * rotates the activations instead of inverse-rotating the weights, since
+ * (W^' Pi) x = W^' (Pi x); the rotation ablation of the OrbitQuant page,
+ * Experiments, times it for RPBH, Block-RHT and the full RHT.
+ * X: device [M, d] F32 or BF16; out: device [M, d], out_dtype F32 or F16
+ * (nearest even).  Errors: ORBIT_E_ARG (null or misaligned pointers),
+ * ORBIT_E_SHAPE (d, h, M), ORBIT_E_DTYPE, ORBIT_E_HIP. */
 orbit_status orbit_rotate(const orbit_rpbh *rot, const void *X, orbit_dtype x_dtype,
                           int64_t M, int64_t d, void *out, orbit_dtype out_dtype,
                           hipStream_t stream);

@@ -52,7 +52,7 @@ class _RPBH(ctypes.Structure):
                 ("perm", ctypes.c_void_p), ("sign_bits", ctypes.c_void_p),
                 ("gather", ctypes.c_void_p), ("flags", ctypes.c_int32)]
 
-RPBH_IDENTITY = 1  # perm is the identity (Block-RHT): rows are read without a gather
+RPBH_IDENTITY = 1  # set by the library's plan builder when perm is the identity (Block-RHT)
 
 
 def _load():
@@ -63,7 +63,7 @@ def _load():
                          ctypes.c_float, ctypes.c_double)
     sig = {
         "orbit_status_string": ([ctypes.c_int], ctypes.c_char_p),
-        "orbit_last_hip_error": ([], ctypes.c_int),
+        "orbit_last_hip_error": ([ctypes.c_void_p], ctypes.c_int),
         "orbit_fit_codebook": ([I32, I32, I32, D, P, P, P, P], ctypes.c_int),
         "orbit_fit_codebook_sphere": ([I32, I32, I32, D, P, P, P, P], ctypes.c_int),
         "orbit_rpbh_gather_len": ([I32, I32], I64),
@@ -99,8 +99,10 @@ lib = _load()
 def _check(status: int, what: str):
     if status != 0:
         msg = lib.orbit_status_string(status).decode()
-        hip = lib.orbit_last_hip_error() if status == 5 else 0
-        raise OrbitError(f"{what}: {msg} (status {status}, hip {hip})")
+        hip = ctypes.c_int(0)
+        if status == 5:
+            lib.orbit_last_hip_error(ctypes.byref(hip))
+        raise OrbitError(f"{what}: {msg} (status {status}, hip {hip.value})")
 
 
 def _ptr(t):
@@ -164,8 +166,9 @@ def fit_codebook(d: int, bits: int, marginal: str = "gauss") -> Codebook:
 
 class Rotation:
     """RPBH rotation parameters on a device: perm (gather order), sign bits, h,
-    and (for d <= 4096, unless plan=False) the gather plan the row kernels
-    read instead of deriving their offsets from perm and the signs."""
+    and (unless plan=False) the gather plan the row kernels read instead of
+    deriving their offsets from perm and the signs.  Building the plan also
+    lets the library set the identity-permutation flag (struct.flags)."""
 
     def __init__(self, perm, signs, h: int, device="cuda", plan: bool = True):
         perm = np.ascontiguousarray(perm, dtype=np.int32)
@@ -177,9 +180,7 @@ class Rotation:
         self.d, self.h = d, int(h)
         self.perm = torch.from_numpy(perm).to(device)
         self.sign_bits = torch.from_numpy(bits.view(np.int32)).to(device)
-        ident = bool(np.array_equal(perm, np.arange(d, dtype=np.int32)))
-        self.struct = _RPBH(d, int(h), self.perm.data_ptr(), self.sign_bits.data_ptr(), None,
-                            RPBH_IDENTITY if ident else 0)
+        self.struct = _RPBH(d, int(h), self.perm.data_ptr(), self.sign_bits.data_ptr(), None, 0)
         self.gather = None
         n = lib.orbit_rpbh_gather_len(d, int(h)) if plan else 0
         if n > 0:

@@ -7,6 +7,9 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "liborbit.so")
+# measured roofline ceilings for bench.py (not part of the layer's C ABI)
+PEAKS_SOURCES = ["peaks.hip"]
+PEAKS_OUT = os.path.join(HERE, "libpeaks.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["abi.cpp", "codebook.cpp", "rpbh_quant.hip", "rpbh_bf16_act.hip",
@@ -23,8 +26,19 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
          "-Wall", "-Wno-unused-function"]
 
 
-def _compile(src, objdir):
+def _newest_header():
+    inc = os.path.join(os.path.dirname(HERE), "include")
+    paths = [os.path.join(d, f) for d in (CSRC, inc) if os.path.isdir(d)
+             for f in os.listdir(d) if f.endswith(".h")]
+    return max((os.path.getmtime(p) for p in paths), default=0.0)
+
+
+def _compile(src, objdir, incremental=False, headers_mtime=0.0):
     obj = os.path.join(objdir, os.path.basename(src) + ".o")
+    if incremental and os.path.exists(obj):
+        t = os.path.getmtime(obj)
+        if t > os.path.getmtime(os.path.join(CSRC, src)) and t > headers_mtime:
+            return obj
     cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -32,22 +46,30 @@ def _compile(src, objdir):
     return obj
 
 
-def build(verbose=False):
+def build(verbose=False, incremental=False):
+    """Compiles every source (incremental=True: only those whose object is
+    older than the source or any header) and links liborbit.so."""
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
+    hdr = _newest_header()
     with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, objdir), SOURCES))
-    tmp = OUT + ".tmp"
-    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, OUT)
+        objs = list(ex.map(lambda s: _compile(s, objdir, incremental, hdr), SOURCES))
+    _link(objs, OUT)
+    _link([_compile(s, objdir, incremental, hdr) for s in PEAKS_SOURCES], PEAKS_OUT)
     if verbose:
-        print(f"built {OUT}")
+        print(f"built {OUT} and {PEAKS_OUT}")
     return OUT
 
 
+def _link(objs, out):
+    tmp = out + ".tmp"
+    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link of {out} failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, out)
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, incremental="--incremental" in sys.argv)
     sys.exit(0)

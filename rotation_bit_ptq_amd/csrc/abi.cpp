@@ -3,6 +3,7 @@
 // returns an error code with nothing enqueued.
 #include <cmath>
 #include <cstdint>
+#include <vector>
 
 #include "orbit_internal.h"
 
@@ -26,6 +27,12 @@ orbit_status check_rot(const orbit_rpbh* rot, int64_t d) {
   if (!pow2(rot->h) || rot->h < 16 || rot->h > 4096 || d % rot->h) return ORBIT_E_SHAPE;
   if (rot->h > 1024 && d > 4096) return ORBIT_E_SHAPE;  // long blocks: rows kept in registers
   return ORBIT_OK;
+}
+
+// The identity hint counts only with the plan that orbit_rpbh_build_gather
+// built (and whose flags it derived from perm).
+bool identity_hint(const orbit_rpbh* rot) {
+  return rot->gather != nullptr && (rot->flags & ORBIT_RPBH_IDENTITY) != 0;
 }
 
 bool code_bits(int b) { return b == 1 || b == 2 || b == 3 || b == 4 || b == 6 || b == 8; }
@@ -99,7 +106,7 @@ orbit_status group_pack(orbit::RowMode mode, const orbit_rpbh* rot, const void* 
   job.h = rot->h;
   job.perm = rot->perm;
   job.gather = rot->gather;
-  job.perm_identity = (rot->flags & ORBIT_RPBH_IDENTITY) != 0;
+  job.perm_identity = identity_hint(rot);
   job.sign_bits = rot->sign_bits;
   job.in = W;
   job.group = group;
@@ -210,7 +217,11 @@ const char* orbit_status_string(orbit_status status) {
   return "unknown status";
 }
 
-int orbit_last_hip_error(void) { return g_last_hip_error; }
+orbit_status orbit_last_hip_error(int* hip_error_out) {
+  if (!hip_error_out) return ORBIT_E_ARG;
+  *hip_error_out = g_last_hip_error;
+  return ORBIT_OK;
+}
 
 int64_t orbit_rpbh_gather_len(int32_t d, int32_t h) {
   if (d < 16 || d > ORBIT_MAX_D || !pow2(h) || h < 16 || h > 4096 || d % h) return 0;
@@ -218,13 +229,22 @@ int64_t orbit_rpbh_gather_len(int32_t d, int32_t h) {
   return (int64_t)orbit::gather_len(d) + orbit::mfma_words_len(d, h);
 }
 
-orbit_status orbit_rpbh_build_gather(const orbit_rpbh* rot, uint16_t* out, hipStream_t stream) {
+orbit_status orbit_rpbh_build_gather(orbit_rpbh* rot, uint16_t* out, hipStream_t stream) {
   if (!rot) return ORBIT_E_ARG;
   orbit_rpbh plain = *rot;
   plain.gather = nullptr;
   orbit_status st = check_rot(&plain, rot->d);
   if (st != ORBIT_OK) return st;
   if (!out || !aligned16(out)) return ORBIT_E_ARG;
+  // the identity hint is derived here from perm itself, never trusted
+  std::vector<int32_t> host((size_t)rot->d);
+  hipError_t e = hipMemcpyAsync(host.data(), rot->perm, host.size() * sizeof(int32_t),
+                                hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_status(e);
+  bool ident = true;
+  for (int32_t k = 0; k < rot->d && ident; ++k) ident = host[(size_t)k] == k;
+  rot->flags = ident ? ORBIT_RPBH_IDENTITY : 0;
   return hip_status(orbit::launch_gather_plan(rot->d, rot->h, rot->perm, rot->sign_bits, out, stream));
 }
 
@@ -245,7 +265,7 @@ orbit_status orbit_pack_weights(const orbit_rpbh* rot, const orbit_codebook* cw,
   job.h = rot->h;
   job.perm = rot->perm;
   job.gather = rot->gather;
-  job.perm_identity = (rot->flags & ORBIT_RPBH_IDENTITY) != 0;
+  job.perm_identity = identity_hint(rot);
   job.sign_bits = rot->sign_bits;
   job.in = W;
   job.bits = cw->bits;
@@ -274,7 +294,7 @@ orbit_status orbit_quant_act(const orbit_rpbh* rot, const orbit_codebook* ca, co
   job.h = rot->h;
   job.perm = rot->perm;
   job.gather = rot->gather;
-  job.perm_identity = (rot->flags & ORBIT_RPBH_IDENTITY) != 0;
+  job.perm_identity = identity_hint(rot);
   job.sign_bits = rot->sign_bits;
   job.in = X;
   job.bits = ca->bits;
@@ -302,7 +322,7 @@ orbit_status orbit_rotate(const orbit_rpbh* rot, const void* X, orbit_dtype x_dt
   job.h = rot->h;
   job.perm = rot->perm;
   job.gather = rot->gather;
-  job.perm_identity = (rot->flags & ORBIT_RPBH_IDENTITY) != 0;
+  job.perm_identity = identity_hint(rot);
   job.sign_bits = rot->sign_bits;
   job.in = X;
   if (out_dtype == ORBIT_F32) job.xrot_f32_out = (float*)out; else job.rot_out = out;

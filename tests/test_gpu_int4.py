@@ -13,7 +13,7 @@ import torch
 import oracle
 import synth
 from oracle import int4
-from parity import OUT_TOL, as_f64, bits_of, out_f64, rel_fro, to_dev
+from parity import OUT_TOL, as_f64, bits_of, check_group_codes, out_f64, rel_fro, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -25,27 +25,12 @@ SAME_X_TOL = 2.0 ** -11
 
 
 def _check_pack(q_dev, sc_dev, W, perm, signs, h, group=128):
-    ref = int4.int4_pack(W, perm, signs, h, group, "f32")
-    got_s = bits_of(sc_dev)
-    s_bad = got_s != ref["scale_f16"]
-    assert s_bad.mean() < 1e-3, s_bad.mean()
+    wrot = oracle.rpbh_rotate(W, perm, signs, h)
     packed = q_dev.cpu().numpy()
     q = int4.unpack_nibbles(packed, W.shape[1])
-    bad = q != ref["q"]
-    # codes differ only where w'/scale sits on a half-integer: the kernel's
-    # float32 w' differs from float32(exact w') by ~1e-7 of the group's max,
-    # i.e. ~1e-6 in units of the scale (max/7)
-    wr = ref["wrot"].reshape(q.shape[0], -1, group)
-    sc64 = oracle.f16_bits_to_f64(ref["scale_f16"])[..., None]
-    with np.errstate(invalid="ignore", divide="ignore"):
-        ratio = np.where(sc64 > 0, wr / sc64, 0.0).reshape(q.shape)
-    frac = np.abs(np.abs(ratio - np.floor(ratio)) - 0.5)
-    gs = np.repeat(s_bad, group, axis=1)
-    assert np.all(frac[bad & ~gs] <= 1e-5)
-    assert bad.mean() < 1e-4
-    # the bytes themselves: two's-complement nibbles, low first
-    same = ~bad.reshape(q.shape[0], -1, 2).any(-1)
-    assert np.array_equal(packed[same], int4.pack_nibbles(ref["q"])[same])
+    check_group_codes(q, bits_of(sc_dev), wrot, group, int4.QMAX, f"int4-K{W.shape[1]}-h{h}")
+    # the bytes themselves: two's-complement nibbles, code 2j in the low nibble
+    assert np.array_equal(packed, int4.pack_nibbles(q))
     return q
 
 
@@ -132,6 +117,7 @@ def test_int4_rejects_bad_shapes(gpu_lib):
 # (4096, 2049, 384) has an odd number of scale entries and takes the
 # register-fed kernel instead.
 STAGED = [(4096, 2048, 512), (4000, 2100, 256), (4096, 2048, 128), (4096, 2049, 384),
+          (4096, 2048, 4096),   # the int8 workload's K
           # narrow batches (M <= 32: one workgroup per 32 weight rows; 64: small tiles)
           (16, 4608, 3072), (64, 1000, 1024), (5, 33, 128)]
 
@@ -151,3 +137,21 @@ def test_int4_linear_staged_tiles(gpu_lib, M, N, K):
     assert rel_fro(out_f64(out32), y) < SAME_X_TOL
     out16 = rbp.int4_linear(xr, q, sc, 128, bias=bias)
     assert rel_fro(out_f64(out16), y) < OUT_TOL
+
+
+def test_int4_workload_full_size_sampled(gpu_lib):
+    """The int8 workload's shape with 4-bit codes (16384 tokens, 4096 -> 4096,
+    h = 128), sampled outputs against the literal oracle."""
+    rbp = gpu_lib
+    inp = synth.make(3)
+    rot = rbp.Rotation(inp["perm"], inp["signs"], 128)
+    q, sc = rbp.int4_pack_weights(rot, to_dev(inp["W"]), 128)
+    xr = rbp.rotate(rot, to_dev(inp["X"]), torch.float16)
+    out = rbp.int4_linear(xr, q, sc, 128)
+    g = np.random.default_rng(9)
+    ms = np.sort(g.choice(inp["M"], 64, replace=False))
+    ns = np.sort(g.choice(inp["N"], 96, replace=False))
+    qi = int4.unpack_nibbles(q[ns].cpu().numpy(), inp["K"])
+    y, _ = int4.int4_linear(as_f64(inp["X"][ms]), qi, bits_of(sc[ns]), inp["perm"],
+                            inp["signs"], 128)
+    assert rel_fro(out_f64(out[ms][:, ns]), y) < OUT_TOL

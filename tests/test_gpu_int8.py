@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import synth
-from parity import OUT_TOL, as_f64, bits_of, out_f64, rel_fro, to_dev
+from parity import OUT_TOL, as_f64, bits_of, check_group_codes, out_f64, rel_fro, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -76,24 +76,14 @@ def test_rotate_f16_matrix_core_shapes(gpu_lib, d, h, ident):
     _check_f16_rotation(x16, ref)
 
 
-def test_int8_pack_matches_oracle(gpu_lib):
+@pytest.mark.parametrize("N", [300, 4096])
+def test_int8_pack_matches_oracle(gpu_lib, N):
+    # N = 4096: the full 4096 x 4096 weight of the int8 workload
     rbp = gpu_lib
-    inp, rot = _setup(rbp, N=300)
+    inp, rot = _setup(rbp, M=8, N=N)
     q, sc = rbp.int8_pack_weights(rot, to_dev(inp["W"]), 128)
-    ref = oracle.int8_pack(as_f64(inp["W"]), inp["perm"], inp["signs"], inp["h"], 128, "f32")
-    got_s = bits_of(sc)
-    s_bad = got_s != ref["scale_f16"]
-    assert s_bad.mean() < 1e-3, s_bad.mean()
-    q = q.cpu().numpy()
-    bad = q != ref["q"]
-    # mismatching codes only where w'/scale sits on a half-integer within 1e-6
-    wr = ref["wrot"].reshape(q.shape[0], -1, 128)
-    sc64 = oracle.f16_bits_to_f64(ref["scale_f16"])[..., None]
-    ratio = (wr / sc64).reshape(q.shape)
-    frac = np.abs(np.abs(ratio - np.floor(ratio)) - 0.5)
-    gs = np.repeat(s_bad, 128, axis=1)
-    assert np.all(frac[bad & ~gs] <= 1e-4)   # fp32 w' error ~1e-7 of amax, times 127
-    assert bad.mean() < 1e-4
+    wrot = oracle.rpbh_rotate(as_f64(inp["W"]), inp["perm"], inp["signs"], inp["h"])
+    check_group_codes(q.cpu().numpy(), bits_of(sc), wrot, 128, 127, f"int8-pack-N{N}")
 
 
 def test_int8_linear_matches_literal_oracle(gpu_lib):
@@ -128,6 +118,8 @@ def test_int8_linear_ragged(gpu_lib, M, N):
 # from the exact product only by the fp16 rounding of each decoded weight
 # (relative <= 2^-11) and fp32 accumulation.
 STAGED = [(4096, 2048, 512), (4000, 2100, 256), (4096, 2048, 128), (4096, 2049, 384),
+          (4096, 2048, 4096),   # the int8 workload's K
+
           # narrow batches (M <= 32: one workgroup per 32 weight rows; 64: small tiles)
           (16, 4608, 3072), (64, 1000, 1024), (5, 33, 128)]
 
@@ -147,3 +139,27 @@ def test_int8_linear_staged_tiles(gpu_lib, M, N, K):
     assert rel_fro(out_f64(out32), y) < 2.0 ** -11
     out16 = rbp.int8_linear(xr, q, sc, 128, bias=bias)
     assert rel_fro(out_f64(out16), y) < OUT_TOL
+
+
+def test_int8_workload_full_size_sampled(gpu_lib):
+    """The int8 workload at its full size (16384 tokens, 4096 -> 4096, h = 128)
+    in the launch the benchmark times: sampled outputs against the literal
+    dequantize -> inverse-rotate -> X W^T oracle, and against the exact
+    product on the GPU's own fp16 x'."""
+    from oracle.int8 import int8_linear_rotated
+    rbp = gpu_lib
+    inp, rot = _setup(rbp, M=16384, N=4096)
+    q, sc = rbp.int8_pack_weights(rot, to_dev(inp["W"]), 128)
+    xr = rbp.rotate(rot, to_dev(inp["X"]), torch.float16)
+    out = rbp.int8_linear(xr, q, sc, 128)
+    g = np.random.default_rng(8)
+    ms = np.sort(g.choice(16384, 64, replace=False))
+    ns = np.sort(g.choice(4096, 96, replace=False))
+    qn, scn = q[ns].cpu().numpy(), bits_of(sc[ns])
+    got = out_f64(out[ms][:, ns])
+    y, _ = oracle.int8_linear(as_f64(inp["X"][ms]), qn, scn, inp["perm"], inp["signs"],
+                              inp["h"], 128)
+    assert rel_fro(got, y) < OUT_TOL
+    x16 = oracle.f16_bits_to_f64(bits_of(xr[ms]))
+    y16 = int8_linear_rotated(x16, qn, scn, 128)
+    assert rel_fro(got, y16) < OUT_TOL

@@ -171,3 +171,19 @@ def test_status_strings():
 ])
 def test_gather_plan_length(d, h, expect):
     assert _lib().lib.orbit_rpbh_gather_len(d, h) == expect
+
+
+def test_last_hip_error_reports_through_pointer():
+    lib = _lib().lib
+    assert lib.orbit_last_hip_error(None) == 1            # ORBIT_E_ARG
+    code = ctypes.c_int(-1)
+    assert lib.orbit_last_hip_error(ctypes.byref(code)) == 0
+    assert code.value == 0                                # no failed HIP call on this thread
+
+
+def test_build_gather_refuses_bad_arguments_before_any_hip_call():
+    lib = _lib().lib
+    assert lib.orbit_rpbh_build_gather(None, None, None) == 1
+    rot = _rot(d=3072)
+    rot.h = 100
+    assert lib.orbit_rpbh_build_gather(ctypes.byref(rot), ctypes.c_void_p(16), None) == 2

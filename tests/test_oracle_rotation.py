@@ -126,6 +126,25 @@ def test_haar_is_orthogonal():
     np.testing.assert_allclose(Q @ Q.T, np.eye(96), atol=1e-12)
 
 
+def test_haar_distribution_moments():
+    """Haar measure on O(d): every entry has mean 0 and variance 1/d, and the
+    trace has mean 0 and second moment 1 (Diaconis & Shahshahani 1994, the
+    moments of tr Q for Q uniform on O(d), d >= 2).  A QR without the sign
+    correction of R's diagonal fails this: Householder QR gives
+    Q[0, 0] = -|A[0, 0]| / ||A[:, 0]|| <= 0, so the mean of Q[0, 0] would be
+    about -sqrt(2 / (pi d))."""
+    d, n = 6, 4000
+    Qs = np.stack([oracle.haar_matrix(d, 1000 + i) for i in range(n)])
+    q00 = Qs[:, 0, 0]
+    tr = np.trace(Qs, axis1=1, axis2=2)
+    se = np.sqrt(1.0 / d / n)                        # standard error of a mean entry
+    assert abs(q00.mean()) < 5 * se
+    assert np.all(np.abs(Qs.mean(axis=0)) < 5 * se)
+    assert abs((Qs ** 2).mean(axis=0).mean() - 1.0 / d) < 1e-12   # rows are unit vectors
+    assert abs(tr.mean()) < 5 * np.sqrt(1.0 / n)                   # Var(tr Q) = 1
+    assert abs((tr ** 2).mean() - 1.0) < 5 * np.sqrt(2.0 / n)      # E[tr^4] = 3
+
+
 def test_down_permutation_folds_into_up_rows():
     """Pi_down GELU(z) with pi applied to z's rows first is the block
     rotation alone: blkdiag(H D) GELU(P_pi z) = Pi_down GELU(z) (GELU acts
