@@ -41,21 +41,23 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(HERE, "profiles", "traffic.json"),
                     help="per-launch HBM bytes measured with rocprofv3 counters")
-    ap.add_argument("--only", choices=["quant", "gemm", "copy"], default=None,
+    ap.add_argument("--only", choices=["quant", "gemm", "copy", "mfma"], default=None,
                     help="launch only one kernel --steps times (for counter runs): the "
-                         "activation rotate+quantize, the decode GEMM, or a plain device "
-                         "copy of COPY_BYTES that calibrates FETCH_SIZE / WRITE_SIZE")
+                         "activation rotate+quantize, the decode GEMM, a plain device "
+                         "copy of COPY_BYTES that calibrates FETCH_SIZE / WRITE_SIZE, or "
+                         "the matrix-core loop of the measured MFMA ceiling")
     return ap.parse_args()
 
 
 COPY_BYTES = 256 << 20   # calibration copy: 256 MiB read + 256 MiB written per launch
 
 
-def cpu_baseline(inp, gpu_idx, gpu_s, rounds_target_s=12.0, block=512):
+def cpu_baseline(inp, gpu_idx, gpu_s, rounds_target_s=10.0, block=512):
     """The oracle as it stands, on this host's cores: rotate + quantize the
-    activations and the fp64 product from codes, over successive distinct
-    blocks of `block` tokens of the workload until about `rounds_target_s`
-    seconds have passed (the weights are packed once beforehand, untimed).
+    activations and the fp64 product from codes, over the workload's tokens
+    in blocks of `block`, in order, for whole passes over all the tokens
+    until about `rounds_target_s` seconds have passed (at most 30 passes;
+    the weights are packed once beforehand, untimed).
 
     The same leg compares the GPU's activation codes and norms for every
     token the oracle quantized with the oracle's own (the parity rule of the
@@ -84,13 +86,17 @@ def cpu_baseline(inp, gpu_idx, gpu_s, rounds_target_s=12.0, block=512):
         return a
 
     run(0, 64)  # warm-up
-    blocks, elapsed, nb = M // block, 0.0, 0
+    blocks, elapsed, nb, passes = M // block, 0.0, 0, 0
     t0 = time.perf_counter()
     checks = []
-    while elapsed < rounds_target_s and nb < blocks:
-        lo, hi = nb * block, (nb + 1) * block
-        checks.append((lo, hi, run(lo, hi)))
-        nb += 1
+    while passes < 30 and (passes == 0 or elapsed < rounds_target_s):
+        for b in range(blocks):
+            lo, hi = b * block, (b + 1) * block
+            a = run(lo, hi)
+            if passes == 0:
+                checks.append((lo, hi, a))
+            nb += 1
+        passes += 1
         elapsed = time.perf_counter() - t0
     # the parity check, outside the timed oracle work
     for lo, hi, a in checks:
@@ -107,10 +113,11 @@ def cpu_baseline(inp, gpu_idx, gpu_s, rounds_target_s=12.0, block=512):
     flops = 2.0 * tokens * N * K
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(cores),
             "blas_threads": int(blas), "kind": "oracle",
-            "sample": f"the first {tokens} distinct tokens of the {M}-token workload, "
-                      f"{nb} blocks of {block} (rotate + quantize + fp64 product from codes "
-                      f"against all {N} packed weight rows), {elapsed:.1f} s"}, {
-        "tokens_checked": tokens, "codes_checked": n_codes,
+            "sample": f"{passes} whole passes over all {blocks * block} tokens of the workload "
+                      f"in blocks of {block} ({tokens} tokens: rotate + quantize + fp64 "
+                      f"product from codes against all {N} packed weight rows), "
+                      f"{elapsed:.1f} s"}, {
+        "tokens_checked": blocks * block, "codes_checked": n_codes,
         "code_mismatch_frac": mism["f64"] / max(n_codes, 1),
         "code_mismatch_frac_f32_decision": mism["f32"] / max(n_codes, 1),
         "mismatches_outside_band": outside,
@@ -314,6 +321,70 @@ def measured_traffic(entry):
                      entry["write_kib"] * 1024 * entry["write_scale"]))
 
 
+def launch_stats(torch, stream, fn, n):
+    """Kernel time on the launching stream: the mean over n back-to-back
+    launches (events around the whole run, as a kernel trace averages), and
+    the median / p10 / p90 of n launches each bracketed by its own events
+    (those include the events' own overhead)."""
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(n):
+        fn(i)
+    b.record(stream)
+    b.synchronize()
+    mean = a.elapsed_time(b) * 1e3 / n
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for i, (e0, e1) in enumerate(ev):
+        e0.record(stream)
+        fn(i)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in ev])
+    return {"mean_us": round(mean, 3), "median_us": round(float(np.median(t)), 3),
+            "p10_us": round(float(np.percentile(t, 10)), 3),
+            "p90_us": round(float(np.percentile(t, 90)), 3)}
+
+
+def measured_peaks(torch, dev, stream, trips=20000):
+    """Ceilings measured on this device: a plain device copy (HBM read +
+    write) and a loop of fp16 matrix-core products from registers (random
+    normal operands, which set the clock the matrix cores run at under
+    load, and constant ones), with the shader clock over the loop."""
+    import ctypes
+    res = {}
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    st = launch_stats(torch, stream, lambda i: dst.copy_(src), 10)
+    res["copy_gbps"] = round(2 * COPY_BYTES / st["mean_us"] / 1e3, 1)
+    del src, dst
+    lib = ctypes.CDLL(os.path.join(HERE, "rotation_bit_ptq_amd", "libpeaks.so"))
+    lib.peaks_mfma_loop.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p]
+    chains = lib.peaks_mfma_chains()
+    wall_ghz = lib.peaks_wall_clock_khz() * 1e-6
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    g = torch.Generator(device=dev).manual_seed(11)
+    seeds = {"random": torch.randn(4096 * 8, generator=g, device=dev).to(torch.float16),
+             "constant": torch.full((4096 * 8,), 0.5, device=dev, dtype=torch.float16)}
+    sink = torch.empty(n_cu * 2 * 256, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(2, dtype=torch.int64, device=dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    for kind, seed in seeds.items():
+        for wps in (1, 2):
+            run = lambda i: lib.peaks_mfma_loop(ctypes.c_void_p(seed.data_ptr()), trips, wps,  # noqa: E731
+                                                ctypes.c_void_p(sink.data_ptr()),
+                                                ctypes.c_void_p(clocks.data_ptr()), sp)
+            assert run(0) == 0
+            st = launch_stats(torch, stream, run, 5)
+            flops = 2.0 * 32 * 32 * 16 * chains * trips * n_cu * 4 * wps
+            ck = clocks.cpu().numpy()
+            res[f"mfma_{kind}_{wps}w_tflops"] = round(flops / st["mean_us"] / 1e6, 1)
+            res[f"mfma_{kind}_{wps}w_sclk_ghz"] = round(float(ck[0]) / float(ck[1]) * wall_ghz, 3)
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -363,6 +434,9 @@ def main():
 
     if args.only is not None:
         # one kernel alone, for rocprofv3 counter passes (no timing line)
+        if args.only == "mfma":
+            print(json.dumps({"only": "mfma", **measured_peaks(torch, dev, stream)}), flush=True)
+            return
         if args.only == "copy":
             src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
             dst = torch.empty_like(src)
@@ -418,21 +492,15 @@ def main():
     # steps the quantizer's stream has evicted them and a kernel trace shows
     # it ~4 % slower there (the step_*_us fields carry the event-split step
     # figures, which include the events' own overhead).
-    def per_launch(fn, n):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for i in range(n):
-            fn(i)
-        b.record(stream)
-        b.synchronize()
-        return a.elapsed_time(b) * 1e-3 / n
-
     n_kern = max(args.steps, 20)
-    tq = per_launch(lambda i: quant(pool[i % pool_n]), n_kern)
-    tg = per_launch(lambda i: gemm(), n_kern)
+    cold = launch_stats(torch, stream, lambda i: quant(pool[i % pool_n]), n_kern)
+    warm = launch_stats(torch, stream, lambda i: quant(pool[0]), n_kern)
+    gst = launch_stats(torch, stream, lambda i: gemm(), n_kern)
+    tq, tg = cold["mean_us"] * 1e-6, gst["mean_us"] * 1e-6
     gemm_tflops = flops / tg / 1e12
     quant_gbps = quant_bytes / tq / 1e9
+    peaks = measured_peaks(torch, dev, stream)
+    mfma_ceiling = peaks["mfma_random_1w_tflops"]
 
     traffic_gemm = traffic_quant = None
     if os.path.exists(args.traffic):
@@ -461,14 +529,24 @@ def main():
                    "tokens": M, "d_in": K, "d_out": N, "h": h, "bits_a": 4, "bits_w": 4},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_MFMA_F16,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_MFMA_F16, 4),
-                     "traffic": traffic_gemm, "kernel": "orbit_qlinear (codebook-decode GEMM)"},
+                     "traffic": traffic_gemm, "kernel": "orbit_qlinear (codebook-decode GEMM)",
+                     "flops_per_launch": flops,
+                     "peak_measured": mfma_ceiling,
+                     "frac_of_measured": round(gemm_tflops / mfma_ceiling, 4)},
         "roofline_quant": {"bound": "hbm", "achieved": round(quant_gbps, 1), "peak": PEAK_HBM,
                            "unit": "GB/s", "frac": round(quant_gbps / PEAK_HBM, 4),
                            "traffic": traffic_quant,
                            "kernel": "orbit_quant_act (fused rotate + quantize)",
-                           "bytes_per_launch": quant_bytes},
+                           "bytes_per_launch": quant_bytes,
+                           "peak_measured": peaks["copy_gbps"],
+                           "frac_of_measured": round(quant_gbps / peaks["copy_gbps"], 4)},
         "gemm_us": round(tg * 1e6, 2),
         "quant_us": round(tq * 1e6, 2),
+        "quant_cold": cold,
+        "quant_warm": warm,
+        "quant_warm_gbps": round(quant_bytes / warm["mean_us"] / 1e3, 1),
+        "gemm_launch": gst,
+        "measured_peaks": peaks,
         "step_gemm_us": round(tg_step.mean() * 1e6, 2),
         "step_quant_us": round(tq_step.mean() * 1e6, 2),
         "quant_gbps": round(quant_gbps, 1),

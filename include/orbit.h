@@ -132,11 +132,18 @@ int64_t orbit_rpbh_gather_len(int32_t d, int32_t h);
  * s = 64 r + l: k = 16 s + e in general; for h = 64, 128 and 256 (T = h/16
  * lanes per Hadamard block, G = 16/T, p = s mod T, e = G t + i) the order
  * that applies H_h = H_T x H_16 as H_T first: k = 16 (s - p) + 16 t + G p + i.
- * The matrix-core section (when present) follows at entry L as uint32 words:
- * word 4 (64 c + l) + q covers the permuted coordinates k and k + 1, k =
- * 512 c + 32 (l mod 16) + 8 floor(l / 16) + 2 q, as 2 perm[k] | (D_k = -1) <<
- * 15 | 2 perm[k + 1] << 16 | (D_{k+1} = -1) << 31 (byte offsets of the bf16
- * coordinates in the row, and their sign flips).
+ * The matrix-core section (when present) follows at entry L as uint32 words
+ * in the order of the kernel that reads it; each word covers two permuted
+ * coordinates k0, k1 as off(k0) | (D_k0 = -1) << 15 | off(k1) << 16 |
+ * (D_k1 = -1) << 31, off(k) the byte offset of x[perm[k]] in that kernel's
+ * LDS copy of the row.  h = 64: word 4 (64 c + l) + q, k0 = 512 c +
+ * 32 (l mod 16) + 8 floor(l / 16) + 2 q, k1 = k0 + 1, off(k) = 2 perm[k].
+ * h = 128, 256: word 4 (64 o + l) + q holds slots j = 2 q, 2 q + 1 of A
+ * operand o of lane l = 16 kq + r16, slot j being coordinate
+ * 512 o + 128 floor(r16 / 4) + 32 kq + 4 j + (r16 mod 4) for h = 128 and
+ * 1024 floor(o / 2) + 256 floor(r16 / 4) + 64 kq + 8 j + 4 (o mod 2) +
+ * (r16 mod 4) for h = 256; off(k) = 2 p + 16 floor(p / 64) with p = perm[k]
+ * when d <= 12288 (a 16-byte pad after every 64 coordinates), 2 p beyond.
  * Errors: ORBIT_E_ARG (null or misaligned pointers), ORBIT_E_SHAPE (d, h),
  * ORBIT_E_HIP. */
 orbit_status orbit_rpbh_build_gather(orbit_rpbh *rot, uint16_t *out, hipStream_t stream);

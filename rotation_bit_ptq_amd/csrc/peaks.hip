@@ -73,4 +73,12 @@ int peaks_mfma_loop(const void* seed, int trips, int waves_per_simd, float* sink
 
 int peaks_mfma_chains(void) { return kChains; }
 
+// Rate of the wall clock read by the loop, in kHz (0 on error).
+int peaks_wall_clock_khz(void) {
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return 0;
+  return khz;
+}
+
 }  // extern "C"

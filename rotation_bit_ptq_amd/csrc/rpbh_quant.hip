@@ -4,6 +4,7 @@
 #include <cmath>
 
 #include "rpbh_impl.h"
+#include "rpbh_mfma2.h"
 
 namespace orbit {
 
@@ -69,21 +70,32 @@ hipError_t launch_rows(const RowJob& job, hipStream_t stream) {
   // the gather plan serves the kernels whose gather order it was built in
   // (transposed exactly when h allows it)
   if (job.gather && fast == tr_order) a.gather = job.gather;
-  a.mfma_words = job.gather && mfma_words_len(job.d, job.h) > 0
-                     ? (const uint32_t*)(job.gather + gather_len(job.d)) : nullptr;
-  // bf16 rows with h = 64, 128 or 256 and d = 1024, 2048, 3072, 4096 (one
-  // wave per row) or 8192, 12288, 16384 (one workgroup per row), codebook
-  // modes: the Hadamard runs on the matrix cores.  Measured on MI355X, with
-  // the rotation's plan (offset words read, not built per wave) it beats the
-  // butterfly kernels at every size measured (4096 x 3072: 11.8 against
-  // 14.0 us); without the plan it is 4 % behind at 16 rows of 3072 per
-  // compute unit and ahead above that.  The choice does not depend on the
-  // plan, so results never do.
+  const uint32_t* words = job.gather && mfma_words_len(job.d, job.h) > 0
+                              ? (const uint32_t*)(job.gather + gather_len(job.d)) : nullptr;
+  const bool rot_f16 = job.mode == RowMode::kRotate && job.out_dtype == ORBIT_F16;
+  // bf16 rows with h = 128 or 256 and d = 1024 .. 4096 (one wave per row) or
+  // 8192, 12288, 16384 (four waves per row): the Hadamard runs on the
+  // matrix cores and each lane packs and stores its own runs of codes
+  // (rpbh_mfma2.h), reading the plan's offset words in that kernel's order
+  // when the rotation has a plan.
+  if (bf16 && ((quant && m2_takes(job.d, job.h, job.bits, false)) ||
+               (rot_f16 && m2_takes(job.d, job.h, 0, true)))) {
+    a.mfma_words = words;
+    const bool act = job.mode == RowMode::kActQuant;
+    if (job.h == 128) {
+      if (rot_f16) return launch_m2<kRotF16, 4>(a, 0, stream);
+      return act ? launch_m2<kAct, 4>(a, job.bits, stream) : launch_m2<kWeight, 4>(a, job.bits, stream);
+    }
+    if (rot_f16) return launch_m2<kRotF16, 8>(a, 0, stream);
+    return act ? launch_m2<kAct, 8>(a, job.bits, stream) : launch_m2<kWeight, 8>(a, job.bits, stream);
+  }
+  // The first matrix-core kernels (rpbh_mfma.h) stage codes in LDS: h = 64,
+  // and 3-bit codes with h = 128.  The plan's words are in their order only
+  // for h = 64; otherwise they build their offsets from pi and the signs.
+  a.mfma_words = job.h == 64 ? words : nullptr;
   const bool mfma = fast && quant &&
                     ((job.d % 1024 == 0 && job.d <= 4096) || job.d == 8192 || job.d == 12288 || job.d == 16384);
-  // the fp16 rotation of such rows, likewise
-  const bool mfma_rot = fast && job.mode == RowMode::kRotate && job.out_dtype == ORBIT_F16 &&
-                        job.d % 1024 == 0 && job.d <= 4096;
+  const bool mfma_rot = fast && rot_f16 && job.d % 1024 == 0 && job.d <= 4096;
   if (mfma_rot) {
     if (job.h == 64) return launch_mfma<kRotF16, 2>(a, 0, stream);
     if (job.h == 128) return launch_mfma<kRotF16, 4>(a, 0, stream);
@@ -168,27 +180,45 @@ __global__ __launch_bounds__(256) void gather_plan_kernel(int d, const int32_t* 
   out[i] = (uint16_t)v;
 }
 
-// The plan's matrix-core section: word 4 (64 c + l) + q serves lane l of
-// pair c (positions 512 c .. + 511), element pair 2 q, 2 q + 1 of the lane's
+// The plan's matrix-core section, in the order of the kernel that reads it.
+// h = 64 (rpbh_mfma.h): word 4 (64 c + l) + q serves lane l of pair c
+// (positions 512 c .. + 511), element pair 2 q, 2 q + 1 of the lane's
 // fragment, i.e. permuted coordinates k and k + 1 with k = 512 c + 32 (l %
-// 16) + 8 (l / 16) + 2 q: byte offsets 2 pi(k) and 2 pi(k + 1) in the low
-// and high halves, their sign flips in bits 15 and 31.
-__global__ __launch_bounds__(256) void mfma_words_kernel(int d, const int32_t* perm,
+// 16) + 8 (l / 16) + 2 q: byte offsets 2 pi(k) and 2 pi(k + 1) of the
+// unpadded row in the low and high halves, their sign flips in bits 15 and
+// 31.  h = 128, 256 (rpbh_mfma2.h): word 4 (64 o + l) + q serves lane l of
+// A operand o, slots 2 q and 2 q + 1 (m2::slot_k), with the byte offsets of
+// that kernel's row layout (padded up to 12288 coordinates).
+__global__ __launch_bounds__(256) void mfma_words_kernel(int d, int h, const int32_t* perm,
                                                          const uint32_t* sign_bits, uint32_t* out) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= d / 2) return;
-  const int c = i >> 8, l = (i >> 2) & 63, q = i & 3;
-  const int k = 512 * c + 32 * (l & 15) + 8 * (l >> 4) + 2 * q;
-  const uint32_t s0 = (sign_bits[k >> 5] >> (k & 31)) & 1u;
-  const uint32_t s1 = (sign_bits[(k + 1) >> 5] >> ((k + 1) & 31)) & 1u;
-  out[i] = ((uint32_t)perm[k] * 2u) | ((uint32_t)perm[k + 1] << 17) | (s0 << 15) | (s1 << 31);
+  const int o = i >> 8, l = (i >> 2) & 63, q = i & 3;
+  int k0, k1;
+  uint32_t a0, a1;
+  if (h == 64) {
+    k0 = 512 * o + 32 * (l & 15) + 8 * (l >> 4) + 2 * q;
+    k1 = k0 + 1;
+    a0 = (uint32_t)perm[k0] * 2u;
+    a1 = (uint32_t)perm[k1] * 2u;
+  } else {
+    const int kq = l >> 4, r16 = l & 15;
+    k0 = h == 128 ? rows::m2::slot_k<4>(o, kq, r16, 2 * q) : rows::m2::slot_k<8>(o, kq, r16, 2 * q);
+    k1 = h == 128 ? rows::m2::slot_k<4>(o, kq, r16, 2 * q + 1) : rows::m2::slot_k<8>(o, kq, r16, 2 * q + 1);
+    const bool pad = rows::m2::padded(d);
+    a0 = pad ? rows::m2::row_addr<true>(perm[k0]) : rows::m2::row_addr<false>(perm[k0]);
+    a1 = pad ? rows::m2::row_addr<true>(perm[k1]) : rows::m2::row_addr<false>(perm[k1]);
+  }
+  const uint32_t s0 = (sign_bits[k0 >> 5] >> (k0 & 31)) & 1u;
+  const uint32_t s1 = (sign_bits[k1 >> 5] >> (k1 & 31)) & 1u;
+  out[i] = a0 | (s0 << 15) | (a1 << 16) | (s1 << 31);
 }
 
 hipError_t launch_gather_plan(int d, int h, const int32_t* perm, const uint32_t* sign_bits,
                               uint16_t* out, hipStream_t stream) {
   if (mfma_words_len(d, h) > 0)
-    hipLaunchKernelGGL(mfma_words_kernel, dim3((d / 2 + 255) / 256), dim3(256), 0, stream, d, perm, sign_bits,
-                       (uint32_t*)(out + gather_len(d)));
+    hipLaunchKernelGGL(mfma_words_kernel, dim3((d / 2 + 255) / 256), dim3(256), 0, stream, d, h, perm,
+                       sign_bits, (uint32_t*)(out + gather_len(d)));
   const dim3 grid(gather_len(d) / 256), block(256);
   if (h == 64) hipLaunchKernelGGL(gather_plan_kernel<2>, grid, block, 0, stream, d, perm, sign_bits, out);
   else if (h == 128) hipLaunchKernelGGL(gather_plan_kernel<3>, grid, block, 0, stream, d, perm, sign_bits, out);

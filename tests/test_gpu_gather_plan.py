@@ -38,21 +38,47 @@ def _plan_reference(perm, signs, h, rounds=4):
     return out
 
 
+def _row_byte(p, d):
+    """Byte offset of coordinate p in the LDS row of the h = 128 / 256
+    matrix-core kernels: two bytes per bf16 and, for rows of up to 12288
+    coordinates, a 16-byte pad after every 64."""
+    return 2 * p + (16 * (p // 64) if d <= 12288 else 0)
+
+
 def _words_reference(perm, signs, h):
-    """The documented matrix-core section: word 4 (64 c + l) + q covers
-    permuted coordinates k, k + 1 with k = 512 c + 32 (l % 16) + 8 (l // 16)
-    + 2 q; empty unless h is 64, 128 or 256 and d % 512 == 0."""
+    """The documented matrix-core section (empty unless h is 64, 128 or 256
+    and d % 512 == 0).  h = 64: word 4 (64 c + l) + q covers permuted
+    coordinates k, k + 1 with k = 512 c + 32 (l % 16) + 8 (l // 16) + 2 q, at
+    byte offsets 2 pi(k).  h = 128 / 256: word 4 (64 o + l) + q covers slots
+    j = 2 q, 2 q + 1 of A operand o for lane l = 16 kq + r16, the permuted
+    coordinate of slot j being 512 o + 128 (r16 // 4) + 32 kq + 4 j + r16 % 4
+    (h = 128) or 1024 (o // 2) + 256 (r16 // 4) + 64 kq + 8 j + 4 (o % 2) +
+    r16 % 4 (h = 256), at the padded row's byte offsets."""
     d = perm.shape[0]
     if h not in (64, 128, 256) or d % 512:
         return np.zeros(0, dtype=np.int64)
     out = np.zeros(d // 2, dtype=np.int64)
-    for c in range(d // 512):
+
+    def word(k0, k1, off):
+        return (off(k0) | (int(signs[k0] < 0) << 15) | (off(k1) << 16) | (int(signs[k1] < 0) << 31))
+
+    for o in range(d // 512):
         for lane in range(64):
+            kq, r16 = divmod(lane, 16)
             for q in range(4):
-                k = 512 * c + 32 * (lane % 16) + 8 * (lane // 16) + 2 * q
-                out[4 * (64 * c + lane) + q] = (2 * int(perm[k]) | (int(signs[k] < 0) << 15)
-                                                | (2 * int(perm[k + 1])) << 16
-                                                | (int(signs[k + 1] < 0) << 31))
+                if h == 64:
+                    k = 512 * o + 32 * r16 + 8 * kq + 2 * q
+                    w = word(k, k + 1, lambda k: 2 * int(perm[k]))
+                else:
+                    ks = []
+                    for j in (2 * q, 2 * q + 1):
+                        if h == 128:
+                            ks.append(512 * o + 128 * (r16 // 4) + 32 * kq + 4 * j + r16 % 4)
+                        else:
+                            ks.append(1024 * (o // 2) + 256 * (r16 // 4) + 64 * kq + 8 * j
+                                      + 4 * (o % 2) + r16 % 4)
+                    w = word(ks[0], ks[1], lambda k: _row_byte(int(perm[k]), d))
+                out[4 * (64 * o + lane) + q] = w
     return out
 
 
@@ -82,11 +108,12 @@ def test_plan_for_long_rows(gpu_lib):
 
 
 @pytest.mark.parametrize("cfg,K,h,bits,f32", [
-    (2, 3072, 128, 4, False),   # transposed-gather kernel, bf16
-    (2, 1024, 64, 2, False),    # matrix-core kernel: words from the plan or from pi
+    (2, 3072, 128, 4, False),   # packed-code matrix-core kernel: words from the plan or from pi
+    (2, 1024, 64, 2, False),    # first matrix-core kernel (h = 64)
     (2, 2048, 256, 6, False),
-    (2, 4096, 128, 3, False),
-    (2, 12288, 256, 4, False),  # matrix-core long-row kernel
+    (2, 4096, 128, 3, False),   # 3-bit codes with h = 128: first matrix-core kernel, words from pi
+    (2, 12288, 256, 4, False),  # packed-code kernel, four waves per row
+    (2, 8192, 256, 3, False),
     (2, 512, 32, 4, False),     # consecutive order, bf16
     (2, 3072, 128, 1, False),   # 1-bit codes: consecutive kernel, plan order differs -> unused
     (1, 256, 64, 4, True),      # fp32 rows: consecutive kernel, plan order differs -> unused
