@@ -116,7 +116,7 @@ orbit_status orbit_last_hip_error(int *hip_error_out);
 /* Length in uint16 entries of the gather plan of a rotation of dimension d
  * and block h: 1024 per round of 1024 coordinates, at least 4096
  * (L = 1024 * max(4, ceil(d / 1024))), plus d entries of matrix-core words
- * when h is 64, 128 or 256 and d is a multiple of 512 (d <= 16384); 0 for
+ * when h is 64 .. 4096 and d is a multiple of 512 (d <= 16384); 0 for
  * invalid d, h.  Host only. */
 int64_t orbit_rpbh_gather_len(int32_t d, int32_t h);
 
@@ -138,9 +138,9 @@ int64_t orbit_rpbh_gather_len(int32_t d, int32_t h);
  * (D_k1 = -1) << 31, off(k) the byte offset of x[perm[k]] in that kernel's
  * LDS copy of the row.  h = 64: word 4 (64 c + l) + q, k0 = 512 c +
  * 32 (l mod 16) + 8 floor(l / 16) + 2 q, k1 = k0 + 1, off(k) = 2 perm[k].
- * h = 128, 256: word 4 (64 o + l) + q holds slots j = 2 q, 2 q + 1 of A
- * operand o of lane l = 16 kq + r16, slot j being coordinate
- * 512 o + 128 floor(r16 / 4) + 32 kq + 4 j + (r16 mod 4) for h = 128 and
+ * h = 128 .. 4096: word 4 (64 o + l) + q holds slots j = 2 q, 2 q + 1 of
+ * A operand o of lane l = 16 kq + r16, slot j being coordinate
+ * 512 o + 128 floor(r16 / 4) + 32 kq + 4 j + (r16 mod 4) for h != 256 and
  * 1024 floor(o / 2) + 256 floor(r16 / 4) + 64 kq + 8 j + 4 (o mod 2) +
  * (r16 mod 4) for h = 256; off(k) = 2 p + 16 floor(p / 64) with p = perm[k]
  * when d <= 12288 (a 16-byte pad after every 64 coordinates), 2 p beyond.

@@ -20,7 +20,7 @@ SOURCES = ["abi.cpp", "codebook.cpp", "rpbh_quant.hip", "rpbh_bf16_act.hip",
            "rpbh_mfma_a64.hip", "rpbh_mfma_a128.hip", "rpbh_mfma_a256.hip", "rpbh_mfma_w64.hip",
            "rpbh_mfma_w128.hip", "rpbh_mfma_w256.hip", "rpbh_mfma_r.hip",
            "rpbh_m2_a128.hip", "rpbh_m2_a256.hip", "rpbh_m2_w128.hip", "rpbh_m2_w256.hip",
-           "rpbh_m2_r.hip", "qgemm.hip", "qgemm_int8.hip",
+           "rpbh_m2_r.hip", "rpbh_m2_big.hip", "qgemm.hip", "qgemm_int8.hip",
            "qgemm_a2.hip", "qgemm_a3.hip", "qgemm_a4.hip", "qgemm_a6.hip", "qgemm_a8.hip"]
 # Packed fp32 VALU instructions are kept out of the generated code.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

@@ -82,10 +82,11 @@ __host__ __device__ inline int gather_len(int d) {
 
 // The plan's second section, after gather_len(d) entries: the matrix-core
 // kernels' packed offset words (two uint16 entries per word, one word per
-// pair of coordinates), for the rotations those kernels can take (the
-// 15-bit byte offsets need d <= 16384).
+// pair of coordinates), for the rotations those kernels can take (h = 64 ..
+// 4096; the 15-bit byte offsets need d <= 16384).
 __host__ __device__ inline int mfma_words_len(int d, int h) {
-  return ((h == 64 || h == 128 || h == 256) && d % 512 == 0 && d <= 16384) ? d : 0;
+  const bool hk = h == 64 || h == 128 || h == 256 || h == 512 || h == 1024 || h == 2048 || h == 4096;
+  return (hk && d % 512 == 0 && d <= 16384) ? d : 0;
 }
 hipError_t launch_gather_plan(int d, int h, const int32_t* perm, const uint32_t* sign_bits,
                               uint16_t* out, hipStream_t stream);

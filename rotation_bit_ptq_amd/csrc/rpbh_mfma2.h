@@ -404,12 +404,220 @@ hipError_t launch_d(const RowArgs& a, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
+
+// ---- blocks of 512 .. 4096 coordinates (the full RHT of the rotation
+// ablation, h = d) on rows of 2048 or 4096 coordinates, one wave per row.
+// In Sylvester order H_h = H_{h/128} (x) H_128 over the position's bits
+// above and below bit 7.  The h = 128 factor runs as above (units of four
+// 128-blocks, block kq of unit u in lane group kq), which leaves each lane
+// all 8 NU values of its positions, NU = d / 512 units.  The factor over the
+// 128-block index q = 4 u + kq (log2(h / 128) bits) then runs as register
+// stages over the unit bits below log2(h / 512), and two butterflies across
+// lanes for the kq bits (lane bits 5 and 4): v_permlane32_swap and
+// v_permlane16_swap exchange the halves (rows of 16) of two registers, after
+// which an add and a subtract give both registers' butterflies, with the
+// two registers' halves transposed: afterwards, register u of lane l holds
+// unit U and lane L with U's bit PA equal to lane bit 5 and L's bit 5 equal
+// to u's bit PA (and likewise bit PB with lane bit 4), PA and PB being the
+// two top unit bits.
+template <int MODE, int BITS, int NU, int LOGH, bool kX>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kX ? 2 : (NU == 8 ? 2 : 3))))
+void big_kernel(RowArgs a) {
+  static_assert(MODE == kAct || MODE == kWeight || MODE == kRotF16, "codebook modes and fp16 x'");
+  static_assert((NU == 4 || NU == 8) && LOGH >= 9 && LOGH <= 12 && (1 << LOGH) <= 512 * NU,
+                "blocks of 512 .. 4096 on rows of 2048 or 4096");
+  constexpr bool kQuant = MODE != kRotF16;
+  constexpr int D = 512 * NU;
+  constexpr int UB = LOGH - 9;               // unit bits inside a block
+  constexpr int PA = NU == 8 ? 2 : 1, PB = PA - 1;
+  constexpr uint32_t kRed = (uint32_t)row_lds_bytes(D);
+  constexpr uint32_t kGrid = kRed + 16u;
+  extern __shared__ __align__(16) char smem[];
+  const int lane = threadIdx.x;
+  const int r16 = lane & 15;
+  const uint32_t gbias = a.grid_bias + kGrid;
+  const u32x4* hp = (const u32x4*)kH32Table.w[lane];
+  const bf16x8 hb0 = __builtin_bit_cast(bf16x8, hp[0]), hb1 = __builtin_bit_cast(bf16x8, hp[1]);
+  u32x4 pre[NU];
+  auto load = [&](long long rr) {
+    const u32x4* src = (const u32x4*)((const char*)a.in + (size_t)rr * D * 2);
+#pragma unroll
+    for (int i = 0; i < NU; ++i) pre[i] = __builtin_nontemporal_load(src + lane + 64 * i);
+  };
+  long long row = blockIdx.x;
+  load(row < a.rows ? row : a.rows - 1);
+  uint32_t w[NU][4];
+  load_words<4, NU, true>(a, 0, lane, w);
+  GridCell* const grid = (GridCell*)(smem + kGrid);
+  float* const thr = (float*)(smem + kGrid + a.grid_bytes);
+  if constexpr (kQuant) {
+    build_grid(a, smem + kGrid);
+    __syncthreads();
+    for (int c = lane; c < a.cells; c += 64) thr[c] = grid[c].t;
+  }
+  const float top = kMagic + (float)(a.cells - 1);
+  const floatx4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+
+  for (; row < a.rows; row += gridDim.x) {
+    float ssx = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      if constexpr (kQuant) ssx = RowRegs<uint16_t, 1>::chunk_sumsq(pre[i], ssx);
+      *(u32x4*)(smem + row_addr<true>(8 * (lane + 64 * i))) = pre[i];
+    }
+    if (row + gridDim.x < a.rows) load(row + gridDim.x);
+    float alpha = 0.0f;
+    if constexpr (kQuant) {
+      alpha = row_alpha<MODE, true>(a, wave_sum(ssx), row, lane);
+      const float inv = 1.0f / alpha;
+      for (int c = lane; c < a.cells; c += 64) grid[c].t = thr[c] * inv;
+    }
+    __syncthreads();  // the row and the row's thresholds are in LDS
+    // the h = 128 factor, unit by unit: v[u][4 hf + e] is position
+    // 512 u + 128 kq + 4 (r16 + 16 hf) + e
+    float v[NU][8];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      uint32_t pr[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) pr[q] = gather_pair(w[u][q]);
+      const bf16x8 av = __builtin_bit_cast(bf16x8, make_uint4(pr[0], pr[1], pr[2], pr[3]));
+      const floatx4 y0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb0, zero, 0, 0, 0);
+      const floatx4 y1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hb1, zero, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[u][e] = y0[e];
+        v[u][4 + e] = y1[e];
+      }
+      group_stages<4>(v[u][0], v[u][1], v[u][2], v[u][3]);
+      group_stages<4>(v[u][4], v[u][5], v[u][6], v[u][7]);
+    }
+    __syncthreads();  // every lane has gathered: the row buffer is free
+    // the unit bits inside a block, in registers
+#pragma unroll
+    for (int b = 0; b < UB; ++b)
+#pragma unroll
+      for (int u = 0; u < NU; ++u)
+        if (!(u & (1 << b)))
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            const float x = v[u][c], y = v[u | (1 << b)][c];
+            v[u][c] = x + y;
+            v[u | (1 << b)][c] = x - y;
+          }
+    // the kq bits across lanes: lane bit 5 with units paired on bit PA,
+    // then lane bit 4 with units paired on bit PB
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+      if (!(u & (1 << PA)))
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[u][c]),
+                                                          __float_as_uint(v[u | (1 << PA)][c]), false, false);
+          const float x = __uint_as_float(r[0]), y = __uint_as_float(r[1]);
+          v[u][c] = x + y;
+          v[u | (1 << PA)][c] = x - y;
+        }
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+      if (!(u & (1 << PB)))
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[u][c]),
+                                                          __float_as_uint(v[u | (1 << PB)][c]), false, false);
+          const float x = __uint_as_float(r[0]), y = __uint_as_float(r[1]);
+          v[u][c] = x + y;
+          v[u | (1 << PB)][c] = x - y;
+        }
+    // position of register (u, hf)'s run in this lane after the exchanges
+    auto run_pos = [&](int u, int hf) {
+      const int U = (u & ~((1 << PA) | (1 << PB))) | (((lane >> 5) & 1) << PA) | (((lane >> 4) & 1) << PB);
+      const int kqL = 2 * ((u >> PA) & 1) + ((u >> PB) & 1);
+      return 512 * U + 128 * kqL + 4 * (r16 + 16 * hf);
+    };
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int p = run_pos(u, hf);
+        if constexpr (!kQuant) {
+          const uint32_t h0 = (uint32_t)f32_to_f16_rne(v[u][4 * hf] * a.inv_sqrt_h) |
+                              ((uint32_t)f32_to_f16_rne(v[u][4 * hf + 1] * a.inv_sqrt_h) << 16);
+          const uint32_t h1 = (uint32_t)f32_to_f16_rne(v[u][4 * hf + 2] * a.inv_sqrt_h) |
+                              ((uint32_t)f32_to_f16_rne(v[u][4 * hf + 3] * a.inv_sqrt_h) << 16);
+          *(u32x2*)(a.xrot_f16 + (size_t)row * D + p) = u32x2{h0, h1};
+        } else {
+          const float cell_a = alpha * a.ga;
+          uint32_t packed = 0;
+#pragma unroll
+          for (int e = 3; e >= 0; --e) {
+            const float x = v[u][4 * hf + e];
+            const GridCell g = *(const GridCell*)(smem + grid_addr(x, cell_a, a.gb, top, gbias));
+            packed = (packed << BITS) | (uint32_t)(g.base + (g.t < x ? 1 : 0));
+          }
+          store_code_bytes<4 * BITS / 8>(a.idx_out + (size_t)row * ((size_t)D * BITS / 8) + (size_t)p * BITS / 8,
+                                         packed);
+          if constexpr (kX) {
+            float* out = a.xrot_f32 + (size_t)row * D + p;
+            *(float4*)out = make_float4(v[u][4 * hf] * a.inv_sqrt_h, v[u][4 * hf + 1] * a.inv_sqrt_h,
+                                        v[u][4 * hf + 2] * a.inv_sqrt_h, v[u][4 * hf + 3] * a.inv_sqrt_h);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int MODE, int BITS, int NU, int LOGH, bool kX>
+hipError_t launch_big_typed(const RowArgs& a, hipStream_t stream) {
+  DeviceInfo di;
+  hipError_t e = device_info(&di);
+  if (e != hipSuccess) return e;
+  const int lds = row_lds_bytes(512 * NU) + 16 + a.grid_bytes + a.grid_bytes / 2;
+  if (lds > di.max_lds) return hipErrorInvalidValue;
+  auto kern = big_kernel<MODE, BITS, NU, LOGH, kX>;
+  static LaunchCache cache;
+  int per_cu = 1;
+  e = prepare_launch(cache, (const void*)kern, 64, lds, &per_cu);
+  if (e != hipSuccess) return e;
+  const long long cap = (long long)di.n_cu * per_cu;
+  const int blocks = (int)(a.rows < cap ? a.rows : cap);
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(64), lds, stream, a);
+  return hipGetLastError();
+}
+
+template <int MODE, int BITS, bool kX>
+hipError_t launch_big(const RowArgs& a, hipStream_t stream) {
+  if (a.d == 2048) {
+    switch (a.h) {
+      case 512: return launch_big_typed<MODE, BITS, 4, 9, kX>(a, stream);
+      case 1024: return launch_big_typed<MODE, BITS, 4, 10, kX>(a, stream);
+      case 2048: return launch_big_typed<MODE, BITS, 4, 11, kX>(a, stream);
+    }
+  } else if (a.d == 4096) {
+    switch (a.h) {
+      case 512: return launch_big_typed<MODE, BITS, 8, 9, kX>(a, stream);
+      case 1024: return launch_big_typed<MODE, BITS, 8, 10, kX>(a, stream);
+      case 2048: return launch_big_typed<MODE, BITS, 8, 11, kX>(a, stream);
+      case 4096: return launch_big_typed<MODE, BITS, 8, 12, kX>(a, stream);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
 }  // namespace m2
 
 // Which rows the packed-code kernels take (bf16 input): h = 128 or 256 and
 // d = 1024, 2048, 3072 (h = 128 or 256 with 3072 % 1024 == 0), 4096, 8192,
 // 12288 or 16384; codes of 2, 4, 6 or 8 bits, and 3 bits when h = 256 (a
 // lane's run of 8 codes is 3 whole bytes); or the fp16 rotation.
+// Blocks of 512 .. 4096 coordinates on rows of 2048 or 4096 (big_kernel):
+// codes of 2, 4, 6 or 8 bits, or the fp16 rotation.
+inline bool m2_big_takes(int d, int h, int bits, bool rot_f16) {
+  if (!(d == 2048 || d == 4096) || h < 512 || h > d) return false;
+  return rot_f16 || bits == 2 || bits == 4 || bits == 6 || bits == 8;
+}
+
 inline bool m2_takes(int d, int h, int bits, bool rot_f16) {
   if (h != 128 && h != 256) return false;
   const bool dok = d == 1024 || d == 2048 || d == 3072 || d == 4096 || d == 8192 || d == 12288 || d == 16384;
@@ -420,6 +628,27 @@ inline bool m2_takes(int d, int h, int bits, bool rot_f16) {
 
 template <int MODE, int G>
 hipError_t launch_m2(const RowArgs& a, int bits, hipStream_t stream);
+template <int MODE>
+hipError_t launch_m2_big(const RowArgs& a, int bits, hipStream_t stream);
+
+#define ORBIT_ROWS_M2_BIG(MODE)                                                              \
+  template <>                                                                              \
+  hipError_t launch_m2_big<MODE>(const RowArgs& a, int bits, hipStream_t s) {              \
+    const bool x = MODE == kAct && a.xrot_f32 != nullptr;                                  \
+    switch (bits) {                                                                        \
+      case 2: return x ? m2::launch_big<MODE, 2, true>(a, s) : m2::launch_big<MODE, 2, false>(a, s); \
+      case 4: return x ? m2::launch_big<MODE, 4, true>(a, s) : m2::launch_big<MODE, 4, false>(a, s); \
+      case 6: return x ? m2::launch_big<MODE, 6, true>(a, s) : m2::launch_big<MODE, 6, false>(a, s); \
+      case 8: return x ? m2::launch_big<MODE, 8, true>(a, s) : m2::launch_big<MODE, 8, false>(a, s); \
+    }                                                                                      \
+    return hipErrorInvalidValue;                                                           \
+  }
+
+#define ORBIT_ROWS_M2_BIG_ROT                                                                \
+  template <>                                                                              \
+  hipError_t launch_m2_big<kRotF16>(const RowArgs& a, int, hipStream_t s) {                \
+    return m2::launch_big<kRotF16, 4, false>(a, s);                                        \
+  }
 
 #define ORBIT_ROWS_M2(MODE, G)                                                               \
   template <>                                                                              \

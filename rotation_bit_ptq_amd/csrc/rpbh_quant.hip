@@ -73,6 +73,16 @@ hipError_t launch_rows(const RowJob& job, hipStream_t stream) {
   const uint32_t* words = job.gather && mfma_words_len(job.d, job.h) > 0
                               ? (const uint32_t*)(job.gather + gather_len(job.d)) : nullptr;
   const bool rot_f16 = job.mode == RowMode::kRotate && job.out_dtype == ORBIT_F16;
+  // blocks of 512 .. 4096 coordinates on rows of 2048 or 4096 (the full
+  // RHT): the h = 128 factor on the matrix cores, the block bits above it
+  // in registers and across lanes (rpbh_mfma2.h, big_kernel)
+  if (bf16 && ((quant && m2_big_takes(job.d, job.h, job.bits, false)) ||
+               (rot_f16 && m2_big_takes(job.d, job.h, 0, true)))) {
+    a.mfma_words = words;
+    if (rot_f16) return launch_m2_big<kRotF16>(a, 0, stream);
+    return job.mode == RowMode::kActQuant ? launch_m2_big<kAct>(a, job.bits, stream)
+                                          : launch_m2_big<kWeight>(a, job.bits, stream);
+  }
   // bf16 rows with h = 128 or 256 and d = 1024 .. 4096 (one wave per row) or
   // 8192, 12288, 16384 (four waves per row): the Hadamard runs on the
   // matrix cores and each lane packs and stores its own runs of codes
@@ -186,8 +196,9 @@ __global__ __launch_bounds__(256) void gather_plan_kernel(int d, const int32_t* 
 // fragment, i.e. permuted coordinates k and k + 1 with k = 512 c + 32 (l %
 // 16) + 8 (l / 16) + 2 q: byte offsets 2 pi(k) and 2 pi(k + 1) of the
 // unpadded row in the low and high halves, their sign flips in bits 15 and
-// 31.  h = 128, 256 (rpbh_mfma2.h): word 4 (64 o + l) + q serves lane l of
-// A operand o, slots 2 q and 2 q + 1 (m2::slot_k), with the byte offsets of
+// 31.  h = 128 .. 4096 (rpbh_mfma2.h): word 4 (64 o + l) + q serves lane l
+// of A operand o, slots 2 q and 2 q + 1 (m2::slot_k, in the h = 256 order
+// for h = 256 and in the h = 128 order otherwise), with the byte offsets of
 // that kernel's row layout (padded up to 12288 coordinates).
 __global__ __launch_bounds__(256) void mfma_words_kernel(int d, int h, const int32_t* perm,
                                                          const uint32_t* sign_bits, uint32_t* out) {
@@ -203,8 +214,8 @@ __global__ __launch_bounds__(256) void mfma_words_kernel(int d, int h, const int
     a1 = (uint32_t)perm[k1] * 2u;
   } else {
     const int kq = l >> 4, r16 = l & 15;
-    k0 = h == 128 ? rows::m2::slot_k<4>(o, kq, r16, 2 * q) : rows::m2::slot_k<8>(o, kq, r16, 2 * q);
-    k1 = h == 128 ? rows::m2::slot_k<4>(o, kq, r16, 2 * q + 1) : rows::m2::slot_k<8>(o, kq, r16, 2 * q + 1);
+    k0 = h != 256 ? rows::m2::slot_k<4>(o, kq, r16, 2 * q) : rows::m2::slot_k<8>(o, kq, r16, 2 * q);
+    k1 = h != 256 ? rows::m2::slot_k<4>(o, kq, r16, 2 * q + 1) : rows::m2::slot_k<8>(o, kq, r16, 2 * q + 1);
     const bool pad = rows::m2::padded(d);
     a0 = pad ? rows::m2::row_addr<true>(perm[k0]) : rows::m2::row_addr<false>(perm[k0]);
     a1 = pad ? rows::m2::row_addr<true>(perm[k1]) : rows::m2::row_addr<false>(perm[k1]);

@@ -46,16 +46,16 @@ def _row_byte(p, d):
 
 
 def _words_reference(perm, signs, h):
-    """The documented matrix-core section (empty unless h is 64, 128 or 256
-    and d % 512 == 0).  h = 64: word 4 (64 c + l) + q covers permuted
+    """The documented matrix-core section (empty unless h is 64 .. 4096 and
+    d % 512 == 0).  h = 64: word 4 (64 c + l) + q covers permuted
     coordinates k, k + 1 with k = 512 c + 32 (l % 16) + 8 (l // 16) + 2 q, at
     byte offsets 2 pi(k).  h = 128 / 256: word 4 (64 o + l) + q covers slots
     j = 2 q, 2 q + 1 of A operand o for lane l = 16 kq + r16, the permuted
     coordinate of slot j being 512 o + 128 (r16 // 4) + 32 kq + 4 j + r16 % 4
-    (h = 128) or 1024 (o // 2) + 256 (r16 // 4) + 64 kq + 8 j + 4 (o % 2) +
-    r16 % 4 (h = 256), at the padded row's byte offsets."""
+    (h = 128, and 512 .. 4096) or 1024 (o // 2) + 256 (r16 // 4) + 64 kq +
+    8 j + 4 (o % 2) + r16 % 4 (h = 256), at the padded row's byte offsets."""
     d = perm.shape[0]
-    if h not in (64, 128, 256) or d % 512:
+    if h not in (64, 128, 256, 512, 1024, 2048, 4096) or d % 512:
         return np.zeros(0, dtype=np.int64)
     out = np.zeros(d // 2, dtype=np.int64)
 
@@ -72,7 +72,7 @@ def _words_reference(perm, signs, h):
                 else:
                     ks = []
                     for j in (2 * q, 2 * q + 1):
-                        if h == 128:
+                        if h != 256:
                             ks.append(512 * o + 128 * (r16 // 4) + 32 * kq + 4 * j + r16 % 4)
                         else:
                             ks.append(1024 * (o // 2) + 256 * (r16 // 4) + 64 * kq + 8 * j
@@ -91,7 +91,8 @@ def _check_plan(rot, perm, signs, h, rounds):
     assert np.array_equal(got[n:].view(np.uint32).astype(np.int64), words)
 
 
-@pytest.mark.parametrize("d,h", [(3072, 128), (1024, 64), (2048, 256), (512, 32), (96, 16)])
+@pytest.mark.parametrize("d,h", [(3072, 128), (1024, 64), (2048, 256), (512, 32), (96, 16),
+                                 (4096, 4096), (2048, 512)])
 def test_plan_layout(gpu_lib, d, h):
     perm, signs = synth.rotation_params(d, 7 + d + h)
     rot = gpu_lib.Rotation(perm, signs, h)
@@ -114,6 +115,8 @@ def test_plan_for_long_rows(gpu_lib):
     (2, 4096, 128, 3, False),   # 3-bit codes with h = 128: first matrix-core kernel, words from pi
     (2, 12288, 256, 4, False),  # packed-code kernel, four waves per row
     (2, 8192, 256, 3, False),
+    (2, 4096, 4096, 4, False),  # full RHT: h = 128 factor on the matrix cores, block bits after
+    (2, 2048, 1024, 6, False),
     (2, 512, 32, 4, False),     # consecutive order, bf16
     (2, 3072, 128, 1, False),   # 1-bit codes: consecutive kernel, plan order differs -> unused
     (1, 256, 64, 4, True),      # fp32 rows: consecutive kernel, plan order differs -> unused

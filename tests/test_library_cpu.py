@@ -165,7 +165,7 @@ def test_status_strings():
     (16384, 128, 16384 + 16384),
     (512, 32, 4096),             # h = 32: no matrix-core kernel, no words
     (96, 16, 4096),              # d not a multiple of 512
-    (2048, 512, 4096),
+    (2048, 512, 4096 + 2048),   # blocks of 512 .. 4096: the h = 128 order of words
     (3072, 100, 0),              # h not a power of two
     (100, 64, 0),                # d not a multiple of h
 ])
