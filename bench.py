@@ -41,11 +41,14 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(HERE, "profiles", "traffic.json"),
                     help="per-launch HBM bytes measured with rocprofv3 counters")
-    ap.add_argument("--only", choices=["quant", "gemm", "copy", "mfma"], default=None,
+    ap.add_argument("--only", choices=["quant", "gemm", "copy", "mfma", "video_quant",
+                                       "video_gemm", "full_rht"], default=None,
                     help="launch only one kernel --steps times (for counter runs): the "
                          "activation rotate+quantize, the decode GEMM, a plain device "
-                         "copy of COPY_BYTES that calibrates FETCH_SIZE / WRITE_SIZE, or "
-                         "the matrix-core loop of the measured MFMA ceiling")
+                         "copy of COPY_BYTES that calibrates FETCH_SIZE / WRITE_SIZE, "
+                         "the matrix-core loop of the measured MFMA ceiling, the video "
+                         "projection's quantizer or GEMM, or the full RHT (h = d = 4096) "
+                         "of the rotation ablation")
     return ap.parse_args()
 
 
@@ -301,6 +304,33 @@ def video_layer(rbp, torch, dev, stream, n=10):
             "gemm_us": round(tg, 2), "gemm_tflops": round(2.0 * M * N * K / tg / 1e6, 1)}
 
 
+def other_kernel(rbp, torch, dev, which):
+    """One launch of the video projection's quantizer or GEMM, or of the full
+    RHT of the rotation ablation, as a function of the step, for the counter
+    passes of --only."""
+    import synth
+    to = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    if which == "full_rht":
+        M, d = 16384, 4096
+        perm, signs = synth.rotation_params(d, 4096)
+        g = torch.Generator(device=dev).manual_seed(3)
+        X = torch.randn((M, d), generator=g, device=dev).to(torch.bfloat16)
+        out = torch.empty((M, d), dtype=torch.float16, device=dev)
+        rot = rbp.Rotation(perm, signs, d)
+        return lambda i: rbp.rotate(rot, X, out_dtype=torch.float16, out=out)
+    inp = synth.make(5)
+    K = inp["K"]
+    X, W = to(inp["X"]), to(inp["W"])
+    rot = rbp.Rotation(inp["perm"], inp["signs"], inp["h"])
+    ca, cw = rbp.Codebook(K, inp["bits_a"]), rbp.Codebook(K, inp["bits_w"])
+    if which == "video_quant":
+        return lambda i: rbp.quant_act(rot, ca, X)
+    iw, r = rbp.pack_weights(rot, cw, W)
+    ia, s = rbp.quant_act(rot, ca, X)
+    out = torch.empty((inp["M"], inp["N"]), dtype=torch.bfloat16, device=dev)
+    return lambda i: rbp.qlinear(ia, s, ca, iw, r, cw, K, out=out)
+
+
 def source_digest(files):
     """sha256 over the kernel sources a traffic measurement was taken with."""
     import hashlib
@@ -443,6 +473,8 @@ def main():
             step = lambda i: dst.copy_(src)  # noqa: E731
         elif args.only == "quant":
             step = lambda i: quant(pool[i % pool_n])  # noqa: E731
+        elif args.only in ("video_quant", "video_gemm", "full_rht"):
+            step = other_kernel(rbp, torch, dev, args.only)
         else:
             quant(pool[0])
             step = lambda i: gemm()  # noqa: E731

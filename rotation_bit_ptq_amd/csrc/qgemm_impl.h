@@ -141,8 +141,17 @@ struct CodeOp {  // packed b-bit codebook indices, LSB-first
       // table [pair of 6-bit indices] of fp16 pairs, one copy for all lanes
       // (4096 entries cannot be replicated per lane: the reads conflict on
       // banks, but two codes per read halve the address work, which bounds
-      // the 6-bit decode; measured 10-15 % faster than one code per read)
-      return lb + (field(48 * s + 12 * l, 12) << 2);
+      // the 6-bit decode; measured 10-15 % faster than one code per read).
+      // The table sits at a multiple of 16 KB: the address is the pair
+      // index shifted into bits 2-13 and OR-ed with the base, one v_bfe and
+      // one v_lshl_or (an align and an and for an index across two words).
+      // The empty asm keeps that form: folded, the extract and the shift
+      // become a shift, an and and an add.  (A lane-permute decode with the
+      // 64 values in a register, free of bank conflicts, measured 10 %
+      // slower on the video projection.)
+      uint32_t p = field(48 * s + 12 * l, 12);
+      asm("" : "+v"(p));
+      return (p << 2) | lb;
     } else {
       static_assert(BITS == 3, "unsupported width");
       // table [pair of 3-bit indices][64 lanes] of fp16 pairs
@@ -559,12 +568,22 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
     form(0, 0);
     gather(0);
     form(0, 1);
-    int c = 0;
-    for (; c + 1 < nchunks; c += 2) {
-      chunk(0, c);
-      chunk(1, c + 1);
+    // Two chunks per trip, buffers 0 and 1 in turn (chunk c in buffer c % 2).
+    // An odd count runs chunk 0 ahead of the loop rather than one chunk
+    // behind it: a loop exit that feeds a further chunk made the compiler
+    // copy every accumulator at each trip for the 3- and 6-bit operands.
+    if ((nchunks & 1) == 0) {
+      for (int c = 0; c < nchunks; c += 2) {
+        chunk(0, c);
+        chunk(1, c + 1);
+      }
+    } else {
+      chunk(0, 0);
+      for (int c = 1; c < nchunks; c += 2) {
+        chunk(1, c);
+        chunk(0, c + 1);
+      }
     }
-    if (c < nchunks) chunk(0, c);
   } else if constexpr (KIND == 1) {
     // Raw codes of chunk c + 1 load into the other of two buffers while chunk
     // c is decoded and multiplied.  Decoded token operands are single-

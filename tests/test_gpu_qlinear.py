@@ -65,6 +65,19 @@ def test_qlinear_widths(gpu_lib, ba, bw):
     assert rel_fro(out_f64(out), ref) < OUT_TOL
 
 
+# K over the kernel's k-chunks (128 for 2- and 4-bit pairs, 64 otherwise):
+# an odd count of 128-chunks runs its first chunk ahead of the paired loop.
+@pytest.mark.parametrize("ba,bw,K", [(4, 4, 128), (4, 4, 384), (2, 4, 640), (4, 2, 1152),
+                                     (6, 4, 384), (3, 3, 640), (8, 4, 384)])
+def test_qlinear_chunk_counts(gpu_lib, ba, bw, K):
+    rbp = gpu_lib
+    inp = synth.make(2, M=300, N=260, K=K, h=128)
+    _, ca, cw, ia, s, iw, r = _codes(rbp, inp["X"], inp["W"], inp["perm"], inp["signs"], 128, ba, bw)
+    out = rbp.qlinear(ia, s, ca, iw, r, cw, K, out_dtype=torch.float32)
+    ref = _oracle_out(ia, s, iw, r, ba, bw, K)
+    assert rel_fro(out_f64(out), ref) < OUT_TOL, (ba, bw, K)
+
+
 @pytest.mark.parametrize("M,N", [(1, 1), (1, 300), (17, 5), (257, 193), (513, 385)])
 def test_qlinear_ragged(gpu_lib, M, N):
     rbp = gpu_lib
