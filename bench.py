@@ -490,14 +490,22 @@ def main():
         gemm()
     torch.cuda.synchronize()
 
-    # the timed steps: nothing but the two launches per step
+    # the timed steps: nothing but the two launches per step (and an event
+    # on the stream at each end, which shows how much of the wall time the
+    # device spent on them and how long the host took to enqueue them)
+    e_first = torch.cuda.Event(enable_timing=True)
+    e_last = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e_first.record(stream)
     for i in range(args.steps):
         quant(pool[i % pool_n])
         gemm()
+    e_last.record(stream)
+    enqueue = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    device_ms_per_step = e_first.elapsed_time(e_last) / args.steps
 
     # the same steps again with events between the kernels, for the split
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
@@ -579,6 +587,8 @@ def main():
         "quant_warm_gbps": round(quant_bytes / warm["mean_us"] / 1e3, 1),
         "gemm_launch": gst,
         "measured_peaks": peaks,
+        "step_device_ms": round(device_ms_per_step, 5),
+        "step_host_enqueue_ms": round(enqueue / args.steps * 1e3, 5),
         "step_gemm_us": round(tg_step.mean() * 1e6, 2),
         "step_quant_us": round(tq_step.mean() * 1e6, 2),
         "quant_gbps": round(quant_gbps, 1),

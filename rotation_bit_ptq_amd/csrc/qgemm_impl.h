@@ -423,7 +423,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
   constexpr int STEPS = KC / 16;
   constexpr int kWM = WavesM<KIND>::value, kWN = 4 / kWM;  // wave grid
   constexpr int TM = 32 * WM * kWM, TN = 32 * WN * kWN;
-  static_assert(TM <= 256 && TN <= 256, "one thread per token and per weight row stages the factors");
+  static_assert(TM <= 256 && TN <= 512, "the 256 threads stage the factors of TM tokens and TN weight rows");
+  constexpr int kNR = (TN + 255) / 256;  // weight-row factors per thread
   const uint32_t lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave % kWM, wn = wave / kWM;
@@ -439,13 +440,20 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
   float* const fr = fs + TM;
   float* const fb = fr + TN;
   const int t = threadIdx.x;
-  float vs = 1.0f, vr = 1.0f, vb = 0.0f;
+  float vs = 1.0f, vr[kNR], vb[kNR];
   {
-    const long long m = (long long)tm * TM + t, n = (long long)tn * TN + t;
+    const long long m = (long long)tm * TM + t;
     if (KIND == 0 && t < TM) vs = m < g.M ? g.s[m] * g.inv_k : 0.0f;
-    if (t < TN) {
-      if (KIND == 0) vr = n < g.N ? __uint_as_float((uint32_t)g.r_bf16[n] << 16) : 0.0f;
-      vb = n < g.N ? load_bias(g, n) : 0.0f;
+#pragma unroll
+    for (int q = 0; q < kNR; ++q) {
+      const int i = t + 256 * q;
+      const long long n = (long long)tn * TN + i;
+      vr[q] = 1.0f;
+      vb[q] = 0.0f;
+      if (i < TN) {
+        if (KIND == 0) vr[q] = n < g.N ? __uint_as_float((uint32_t)g.r_bf16[n] << 16) : 0.0f;
+        vb[q] = n < g.N ? load_bias(g, n) : 0.0f;
+      }
     }
   }
   if constexpr (KIND == 0) {
@@ -453,9 +461,13 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
     if (g.table_a_offset != g.table_b_offset) build_table<OpB::kBits>(smem + g.table_b_offset, g.cent_b);
   }
   if (t < TM) fs[t] = vs;
-  if (t < TN) {
-    fr[t] = vr;
-    fb[t] = vb;
+#pragma unroll
+  for (int q = 0; q < kNR; ++q) {
+    const int i = t + 256 * q;
+    if (i < TN) {
+      fr[i] = vr[q];
+      fb[i] = vb[q];
+    }
   }
   __syncthreads();
   const uint32_t lb_a = OpA::lane_base((uint32_t)g.table_a_offset, lane);
@@ -569,20 +581,22 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
     gather(0);
     form(0, 1);
     // Two chunks per trip, buffers 0 and 1 in turn (chunk c in buffer c % 2).
-    // An odd count runs chunk 0 ahead of the loop rather than one chunk
-    // behind it: a loop exit that feeds a further chunk made the compiler
-    // copy every accumulator at each trip for the 3- and 6-bit operands.
-    if ((nchunks & 1) == 0) {
+    if constexpr (KC == 64) {
+      // K is a multiple of 128 (checked at launch), so 64-k chunks come in
+      // pairs.  No odd chunk behind the loop: with one there (the loop's
+      // exit feeding a further chunk) the compiler copied every accumulator
+      // at each trip for the 3- and 6-bit operands.
       for (int c = 0; c < nchunks; c += 2) {
         chunk(0, c);
         chunk(1, c + 1);
       }
     } else {
-      chunk(0, 0);
-      for (int c = 1; c < nchunks; c += 2) {
-        chunk(1, c);
-        chunk(0, c + 1);
+      int c = 0;
+      for (; c + 1 < nchunks; c += 2) {
+        chunk(0, c);
+        chunk(1, c + 1);
       }
+      if (c < nchunks) chunk(0, c);
     }
   } else if constexpr (KIND == 1) {
     // Raw codes of chunk c + 1 load into the other of two buffers while chunk
@@ -988,6 +1002,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
 
 template <int KIND, class OpA, class OpB, int WM, int WN>
 hipError_t launch_tile(GemmArgs& g, int lds, hipStream_t stream) {
+  if (KIND == 0 && OpA::kChunkK == 64 && g.K % 128 != 0) return hipErrorInvalidValue;  // chunk pairs
   constexpr int kWM = WavesM<KIND>::value, kWN = 4 / kWM;
   constexpr int TM = 32 * WM * kWM, TN = 32 * WN * kWN;
   g.tiles_m = (int)((g.M + TM - 1) / TM);
@@ -1025,6 +1040,11 @@ hipError_t launch_shape(GemmArgs& g, int lds, hipStream_t stream) {
     // tile: each of its blocks is decoded once per sub-step and feeds one
     // MFMA per block of the other operand
     if constexpr (KIND == 0 && OpA::kValu > OpB::kValu) {
+      if constexpr (OpA::kBits == 6) {
+        // 6-bit tokens: their pair table's reads conflict on banks, so the
+        // wider 2 x 6 wave tile feeds each of them to six MFMAs
+        if (tiles(128, 384) >= 768) return launch_tile<KIND, OpA, OpB, 2, 6>(g, lds, stream);
+      }
       if (tiles(128, 256) >= 192) return launch_tile<KIND, OpA, OpB, 2, 4>(g, lds, stream);
     } else {
       if (tiles(256, 128) >= 192) return launch_tile<KIND, OpA, OpB, 4, 2>(g, lds, stream);

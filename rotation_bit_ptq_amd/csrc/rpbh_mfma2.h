@@ -178,26 +178,32 @@ __device__ __forceinline__ void units(const RowArgs& a, long long row, int u0,
     const int u = st / SPU, hf = SPU == 1 ? r : st % SPU;
     return Unit<G>::kPos * (u0 + u) + (32 * G) * kq + RUN * (r16 + 16 * hf);
   };
-  uint32_t pr[NO][4];  // gathered pairs of the next unit
+  // Pipelined values alternate between two register sets by the parity of
+  // their unit or step (the loop is unrolled, so the indices are constants
+  // and nothing is copied from one set to the other): the gathered pairs of
+  // unit u in pr[u & 1]; the values of step s and their grid cells in
+  // uu[s & 1] and g[s & 1], compared and packed during step s + 1.
+  uint32_t pr[2][NO][4];
   auto gather = [&](int u) {
 #pragma unroll
     for (int o = 0; o < NO; ++o)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) pr[o][q] = gather_pair(w[NO * u + o][q]);
+      for (int q = 0; q < 4; ++q) pr[u & 1][o][q] = gather_pair(w[NO * u + o][q]);
   };
   gather(0);
-  bf16x8 av[NO];
-  float uu[8];  // the step's values, compared with the row's rescaled thresholds
-  GridCell g[8];
+  float uu[2][8];
+  GridCell g[2][8];
 #pragma unroll
   for (int st = 0; st <= NS; ++st) {
     float v[8];  // run r: v[RUN r + c] is position run_pos(st, r) + c
     if (st < NS) {
-      if (st % SPU == 0) {  // a new unit: its operands, and the next unit's gathers
+      // a new unit: the next unit's gathers
+      if (st % SPU == 0 && st / SPU + 1 < NU) gather(st / SPU + 1);
+      const int ub = (st / SPU) & 1;
+      bf16x8 av[NO];
 #pragma unroll
-        for (int o = 0; o < NO; ++o) av[o] = __builtin_bit_cast(bf16x8, make_uint4(pr[o][0], pr[o][1], pr[o][2], pr[o][3]));
-        if (st / SPU + 1 < NU) gather(st / SPU + 1);
-      }
+      for (int o = 0; o < NO; ++o)
+        av[o] = __builtin_bit_cast(bf16x8, make_uint4(pr[ub][o][0], pr[ub][o][1], pr[ub][o][2], pr[ub][o][3]));
       floatx4 y0, y1;
       if constexpr (G == 4) {  // both halves of H_32 on the one operand
         y0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[0], hb0, zero, 0, 0, 0);
@@ -220,7 +226,8 @@ __device__ __forceinline__ void units(const RowArgs& a, long long row, int u0,
         Packed packed = 0;
 #pragma unroll
         for (int c = RUN - 1; c >= 0; --c) {
-          const int idx = g[RUN * r + c].base + (g[RUN * r + c].t < uu[RUN * r + c] ? 1 : 0);
+          const GridCell& gc = g[(st - 1) & 1][RUN * r + c];
+          const int idx = gc.base + (gc.t < uu[(st - 1) & 1][RUN * r + c] ? 1 : 0);
           packed = (Packed)(packed << BITS) | (Packed)idx;
         }
         uint8_t* out = a.idx_out + (size_t)row * ((size_t)D * BITS / 8) +
@@ -254,8 +261,8 @@ __device__ __forceinline__ void units(const RowArgs& a, long long row, int u0,
       } else {
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-          uu[c] = v[c];
-          g[c] = *(const GridCell*)(smem + grid_addr(v[c], cell_a, a.gb, top, gbias));
+          uu[st & 1][c] = v[c];
+          g[st & 1][c] = *(const GridCell*)(smem + grid_addr(v[c], cell_a, a.gb, top, gbias));
         }
         if constexpr (kX) {
 #pragma unroll

@@ -154,6 +154,25 @@ def test_layer_full_size_sampled(gpu_lib, label, cfg, ba, bw):
     check_indices(ia[ms], ba, K, ref["u"], oracle.codebook(ba)["thresholds"], label)
 
 
+def test_wide_token_tile_ragged(gpu_lib):
+    """6-bit tokens on enough tiles to take the 2 x 6 wave tile (128 x 384
+    per workgroup), with a ragged last column of tiles: sampled tokens
+    against every output column of the last two tile columns and sampled
+    ones elsewhere."""
+    rbp = gpu_lib
+    M, N, K = 4608, 8192 + 96, 2048
+    inp = synth.make(5, M=M, N=N)
+    _, ca, cw, ia, s, iw, r = _codes(rbp, inp["X"], inp["W"], inp["perm"], inp["signs"],
+                                     inp["h"], 6, 4)
+    out = rbp.qlinear(ia, s, ca, iw, r, cw, K)
+    g = np.random.default_rng(5)
+    ms = np.sort(g.choice(M, 40, replace=False))
+    tail = np.arange((N // 384 - 1) * 384, N)
+    ns = np.unique(np.concatenate([tail, g.choice(N, 64, replace=False)]))
+    sub = _oracle_out(ia[ms], s[ms], iw[ns], r[ns], 6, 4, K)
+    assert rel_fro(out_f64(out[ms][:, ns]), sub) < OUT_TOL
+
+
 def test_deterministic(gpu_lib):
     rbp = gpu_lib
     inp = synth.make(2, M=300, N=200)
