@@ -377,6 +377,57 @@ def launch_stats(torch, stream, fn, n):
             "p90_us": round(float(np.percentile(t, 90)), 3)}
 
 
+def quant_neighbours(torch, dev, stream, quant, gemm, pool, n=40):
+    """The quantizer's launch time (median of launches each bracketed by its
+    own events) alone and right after three different kernels: the GEMM as in
+    the step, a loop of random-operand MFMAs of about the GEMM's length (the
+    matrix cores' load without the GEMM's memory traffic), and a 25 MiB device
+    copy (memory traffic without matrix work).  Microseconds."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(HERE, "rotation_bit_ptq_amd", "libpeaks.so"))
+    lib.peaks_mfma_loop.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p]
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    g = torch.Generator(device=dev).manual_seed(11)
+    seed = torch.randn(4096 * 8, generator=g, device=dev).to(torch.float16)
+    sink = torch.empty(n_cu * 2 * 256, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(2, dtype=torch.int64, device=dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def mfma(trips):
+        assert lib.peaks_mfma_loop(ctypes.c_void_p(seed.data_ptr()), trips, 1,
+                                   ctypes.c_void_p(sink.data_ptr()),
+                                   ctypes.c_void_p(clocks.data_ptr()), sp) == 0
+    src = torch.empty(25 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    gemm()
+    a.record(stream)
+    gemm()
+    b.record(stream)
+    b.synchronize()
+    t_gemm = a.elapsed_time(b) * 1e3
+    a.record(stream)
+    mfma(1000)
+    b.record(stream)
+    b.synchronize()
+    trips = max(50, int(1000 * t_gemm / (a.elapsed_time(b) * 1e3)))
+
+    def timed(pre):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        for i, (e0, e1) in enumerate(ev):
+            if pre is not None:
+                pre()
+            e0.record(stream)
+            quant(pool[i % len(pool)])
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return round(float(np.median([e0.elapsed_time(e1) * 1e3 for e0, e1 in ev])), 2)
+    return {"alone": timed(None), "after_gemm": timed(gemm), "after_mfma_loop": timed(lambda: mfma(trips)),
+            "after_copy_25MiB": timed(lambda: dst.copy_(src)), "unit": "us (median, events per launch)"}
+
+
 def measured_peaks(torch, dev, stream, trips=20000):
     """Ceilings measured on this device: a plain device copy (HBM read +
     write) and a loop of fp16 matrix-core products from registers (random
@@ -594,6 +645,7 @@ def main():
         "quant_gbps": round(quant_gbps, 1),
         "gemm_tflops": round(gemm_tflops, 2),
     }
+    line["quant_after"] = quant_neighbours(torch, dev, stream, quant, gemm, pool)
     line["rotation_ablation"] = rotation_ablation(rbp, torch, dev, stream)
     line["mlp_pair"] = mlp_pair(rbp, torch, dev, stream)
     line["weight_only"] = weight_only(rbp, torch, dev, stream)
