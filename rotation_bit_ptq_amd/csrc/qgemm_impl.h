@@ -1034,6 +1034,13 @@ hipError_t launch_shape(GemmArgs& g, int lds, hipStream_t stream) {
   auto tiles = [&](int tm, int tn) { return ((g.M + tm - 1) / tm) * ((g.N + tn - 1) / tn); };
   constexpr bool kNarrow = KIND == 1 || OpA::kChunkK == 128;
   if constexpr (kNarrow) {
+    if constexpr (KIND == 0) {
+      if constexpr (OpB::kBits == 2) {
+        // 2-bit weights (four values per read): the 2 x 8 wave tile halves
+        // the token-code reads per MFMA against 4 x 3 and fits the registers
+        if (tiles(128, 512) >= 768) return launch_tile<KIND, OpA, OpB, 2, 8>(g, lds, stream);
+      }
+    }
     if (tiles(256, 192) >= 192) return launch_tile<KIND, OpA, OpB, 4, 3>(g, lds, stream);
   } else if constexpr (!(OpA::kLookups + OpB::kLookups >= 16 || (OpA::kBits == 8 && OpB::kBits == 3))) {
     // the operand with the costlier decode gets the shorter side of the wave
@@ -1041,8 +1048,9 @@ hipError_t launch_shape(GemmArgs& g, int lds, hipStream_t stream) {
     // MFMA per block of the other operand
     if constexpr (KIND == 0 && OpA::kValu > OpB::kValu) {
       if constexpr (OpA::kBits == 6) {
-        // 6-bit tokens: their pair table's reads conflict on banks, so the
-        // wider 2 x 6 wave tile feeds each of them to six MFMAs
+        // 6-bit tokens: their pair table's reads conflict on banks, so wider
+        // wave tiles feed each of them to eight (2 x 8) or six (2 x 6) MFMAs
+        if (tiles(128, 512) >= 768) return launch_tile<KIND, OpA, OpB, 2, 8>(g, lds, stream);
         if (tiles(128, 384) >= 768) return launch_tile<KIND, OpA, OpB, 2, 6>(g, lds, stream);
       }
       if (tiles(128, 256) >= 192) return launch_tile<KIND, OpA, OpB, 2, 4>(g, lds, stream);

@@ -154,22 +154,26 @@ def test_layer_full_size_sampled(gpu_lib, label, cfg, ba, bw):
     check_indices(ia[ms], ba, K, ref["u"], oracle.codebook(ba)["thresholds"], label)
 
 
-def test_wide_token_tile_ragged(gpu_lib):
-    """6-bit tokens on enough tiles to take the 2 x 6 wave tile (128 x 384
-    per workgroup), with a ragged last column of tiles: sampled tokens
+@pytest.mark.parametrize("cfg,ba,bw,M,N,TN", [(5, 6, 4, 4608, 8192 + 96, 384),
+                                               (5, 6, 4, 6144, 8192 + 96, 512),
+                                               (4, 4, 2, 12800, 4096 + 40, 512)])
+def test_wide_tile_ragged(gpu_lib, cfg, ba, bw, M, N, TN):
+    """Products with enough tiles to take the wide wave tiles: 2 x 6 (128 x
+    384 per workgroup) or 2 x 8 (128 x 512) for 6-bit tokens, 2 x 8 for
+    2-bit weights; each with a ragged last column of tiles.  Sampled tokens
     against every output column of the last two tile columns and sampled
     ones elsewhere."""
     rbp = gpu_lib
-    M, N, K = 4608, 8192 + 96, 2048
-    inp = synth.make(5, M=M, N=N)
+    inp = synth.make(cfg, M=M, N=N)
+    K = inp["K"]
     _, ca, cw, ia, s, iw, r = _codes(rbp, inp["X"], inp["W"], inp["perm"], inp["signs"],
-                                     inp["h"], 6, 4)
+                                     inp["h"], ba, bw)
     out = rbp.qlinear(ia, s, ca, iw, r, cw, K)
     g = np.random.default_rng(5)
     ms = np.sort(g.choice(M, 40, replace=False))
-    tail = np.arange((N // 384 - 1) * 384, N)
+    tail = np.arange((N // TN - 1) * TN, N)
     ns = np.unique(np.concatenate([tail, g.choice(N, 64, replace=False)]))
-    sub = _oracle_out(ia[ms], s[ms], iw[ns], r[ns], 6, 4, K)
+    sub = _oracle_out(ia[ms], s[ms], iw[ns], r[ns], ba, bw, K)
     assert rel_fro(out_f64(out[ms][:, ns]), sub) < OUT_TOL
 
 
