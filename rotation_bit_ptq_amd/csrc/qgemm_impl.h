@@ -1028,7 +1028,9 @@ hipError_t launch_tile(GemmArgs& g, int lds, hipStream_t stream) {
 // 3-bit codes) hold more raw bits and table addresses per operand, so their
 // widest wave tile is 4 x 2 blocks instead of 4 x 3, and 2 x 2 for the
 // pairs whose registers do not fit 4 x 2 (both operands 6- or 8-bit, or
-// 8-bit tokens with 3-bit weights).
+// 8-bit tokens with 3-bit weights).  Products of at least three tiles per
+// compute unit take 2 x 8 (or 2 x 6) wave tiles where the registers allow
+// them: 6-bit tokens and 2-bit weights.
 template <int KIND, class OpA, class OpB>
 hipError_t launch_shape(GemmArgs& g, int lds, hipStream_t stream) {
   auto tiles = [&](int tm, int tn) { return ((g.M + tm - 1) / tm) * ((g.N + tn - 1) / tn); };
