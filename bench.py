@@ -463,6 +463,20 @@ def measured_peaks(torch, dev, stream, trips=20000):
             ck = clocks.cpu().numpy()
             res[f"mfma_{kind}_{wps}w_tflops"] = round(flops / st["mean_us"] / 1e6, 1)
             res[f"mfma_{kind}_{wps}w_sclk_ghz"] = round(float(ck[0]) / float(ck[1]) * wall_ghz, 3)
+    # LDS reads per compute unit and shader clock (eight waves, independent
+    # reads, no bank conflicts): 4-byte lanes as a decode lookup, 16-byte
+    # lanes as an MFMA operand
+    lib.peaks_lds_read.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+    lsink = torch.empty(n_cu * 512, dtype=torch.int32, device=dev)
+    cyc = torch.zeros(n_cu, dtype=torch.int64, device=dev)
+    for kind, lane_bytes in ((0, 4), (1, 16)):
+        for _ in range(2):
+            assert lib.peaks_lds_read(kind, 2048, ctypes.c_void_p(lsink.data_ptr()),
+                                      ctypes.c_void_p(cyc.data_ptr()), sp) == 0
+        torch.cuda.synchronize()
+        mean_cycles = float(cyc.double().mean().item())
+        res[f"lds_read_b{8 * lane_bytes}_bytes_per_clk_cu"] = round(8 * 2048 * 8 * 64 * lane_bytes / mean_cycles, 1)
     return res
 
 
@@ -655,7 +669,14 @@ def main():
         torch.cuda.synchronize()
         line["cpu_baseline"], line["code_parity"] = cpu_baseline(
             inp, idx_a.cpu().numpy(), s.cpu().numpy().astype(np.float64))
+        cp = line["code_parity"]
+        # the method's bar for the codes: mismatches only inside the 1e-6
+        # decision band, and both fractions below 1e-5
+        cp["within_bar"] = bool(cp["mismatches_outside_band"] == 0 and
+                                cp["code_mismatch_frac"] < 1e-5 and cp["band_frac"] < 1e-5)
     print(json.dumps(line), flush=True)
+    if "code_parity" in line and not line["code_parity"]["within_bar"]:
+        sys.exit("activation codes outside the parity bar: " + json.dumps(line["code_parity"]))
 
 
 if __name__ == "__main__":

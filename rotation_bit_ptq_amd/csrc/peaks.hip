@@ -1,7 +1,8 @@
 // Measured ceilings for the benchmark's roofline denominators: a loop of
 // dense fp16 matrix-core products with operands held in registers (what the
 // decode GEMM could at best sustain on this device, including the clock the
-// matrix cores settle at under load), and the shader clock over that loop.
+// matrix cores settle at under load), the shader clock over that loop, and
+// the LDS read throughput per compute unit for 4- and 16-byte lane reads.
 // Not part of the layer's C ABI: bench.py alone loads this library.
 #include <hip/hip_runtime.h>
 
@@ -53,9 +54,60 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(const uint4* seed, int t
   }
 }
 
+// LDS throughput per compute unit: 8 waves (two per SIMD) each issue
+// `trips` x 8 independent reads (kind 0: 4 bytes per lane, as a decode-table
+// lookup; kind 1: 16 bytes per lane, as an MFMA operand) from distinct 1 KB
+// blocks, every lane in its own bank, and wait once per 8.  cycles[block]:
+// shader clocks over the loop.
+template <int KIND>
+__global__ __launch_bounds__(512) void lds_read_kernel(int trips, unsigned* sink, long long* cycles) {
+  __shared__ __align__(16) char lds[65536];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  for (int i = t; i < 65536 / 4; i += 512) ((unsigned*)lds)[i] = (unsigned)i;
+  __syncthreads();
+  const long long c0 = clock64();
+  uint4 acc = make_uint4(0u, 0u, 0u, 0u);
+  for (int it = 0; it < trips; ++it) {
+    uint4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int blk = (it * 8 + j + w * 3) & 63;  // blocks 0..63: bytes 0 .. 65535
+      if constexpr (KIND == 0) v[j].x = *(const unsigned*)(lds + blk * 1024 + lane * 4);
+      else v[j] = *(const uint4*)(lds + blk * 1024 + lane * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      acc.x += v[j].x;
+      if constexpr (KIND == 1) {
+        acc.y += v[j].y;
+        acc.z += v[j].z;
+        acc.w += v[j].w;
+      }
+    }
+  }
+  const long long c1 = clock64();
+  sink[blockIdx.x * 512 + t] = acc.x + acc.y + acc.z + acc.w;
+  if (t == 0) cycles[blockIdx.x] = c1 - c0;
+}
+
 }  // namespace
 
 extern "C" {
+
+// One 512-thread workgroup per compute unit running lds_read_kernel; sink
+// holds n_cu * 512 uint32, cycles n_cu int64.  Bytes read per workgroup:
+// 8 waves * trips * 8 * (kind 0 ? 256 : 1024).  Returns the HIP status.
+int peaks_lds_read(int kind, int trips, unsigned* sink, long long* cycles, hipStream_t stream) {
+  int dev = 0, n_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return (int)e;
+  if (trips < 1 || (kind != 0 && kind != 1)) return (int)hipErrorInvalidValue;
+  if (kind == 0) hipLaunchKernelGGL(lds_read_kernel<0>, dim3(n_cu), dim3(512), 0, stream, trips, sink, cycles);
+  else hipLaunchKernelGGL(lds_read_kernel<1>, dim3(n_cu), dim3(512), 0, stream, trips, sink, cycles);
+  return (int)hipGetLastError();
+}
+
 
 // waves_per_simd waves on every SIMD of every compute unit; returns the
 // HIP status.  flops per launch = 2 * 32 * 32 * 16 * kChains * trips * waves.
