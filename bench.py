@@ -42,13 +42,15 @@ def parse():
     ap.add_argument("--traffic", default=os.path.join(HERE, "profiles", "traffic.json"),
                     help="per-launch HBM bytes measured with rocprofv3 counters")
     ap.add_argument("--only", choices=["quant", "gemm", "copy", "mfma", "video_quant",
-                                       "video_gemm", "full_rht"], default=None,
+                                       "video_gemm", "full_rht", "w8a16", "w4a16",
+                                       "w8a16_narrow", "w4a16_narrow"], default=None,
                     help="launch only one kernel --steps times (for counter runs): the "
                          "activation rotate+quantize, the decode GEMM, a plain device "
                          "copy of COPY_BYTES that calibrates FETCH_SIZE / WRITE_SIZE, "
                          "the matrix-core loop of the measured MFMA ceiling, the video "
-                         "projection's quantizer or GEMM, or the full RHT (h = d = 4096) "
-                         "of the rotation ablation")
+                         "projection's quantizer or GEMM, the full RHT (h = d = 4096) "
+                         "of the rotation ablation, or a weight-only GEMM (int8 workload, "
+                         "or the AdaLN-style shape with _narrow)")
     return ap.parse_args()
 
 
@@ -305,11 +307,26 @@ def video_layer(rbp, torch, dev, stream, n=10):
 
 
 def other_kernel(rbp, torch, dev, which):
-    """One launch of the video projection's quantizer or GEMM, or of the full
-    RHT of the rotation ablation, as a function of the step, for the counter
-    passes of --only."""
+    """One launch of the video projection's quantizer or GEMM, of the full
+    RHT of the rotation ablation, or of a weight-only GEMM (the int8
+    workload's 16384 x 4096 -> 4096, or the AdaLN-style 16 x 3072 -> 18432
+    with _narrow), as a function of the step, for the counter passes of
+    --only."""
     import synth
     to = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    if which.startswith(("w8a16", "w4a16")):
+        M, K, N = (16, 3072, 18432) if which.endswith("_narrow") else (16384, 4096, 4096)
+        perm, signs = synth.rotation_params(K, 7)
+        g = torch.Generator(device=dev).manual_seed(5)
+        X = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
+        W = (torch.randn((N, K), generator=g, device=dev) / K ** 0.5).to(torch.bfloat16)
+        rot = rbp.Rotation(perm, signs, 128)
+        pack, linear = ((rbp.int8_pack_weights, rbp.int8_linear) if which.startswith("w8")
+                        else (rbp.int4_pack_weights, rbp.int4_linear))
+        q, sc = pack(rot, W, 128)
+        xr = rbp.rotate(rot, X, out_dtype=torch.float16)
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        return lambda i: linear(xr, q, sc, 128, out=out)
     if which == "full_rht":
         M, d = 16384, 4096
         perm, signs = synth.rotation_params(d, 4096)
@@ -538,7 +555,8 @@ def main():
             step = lambda i: dst.copy_(src)  # noqa: E731
         elif args.only == "quant":
             step = lambda i: quant(pool[i % pool_n])  # noqa: E731
-        elif args.only in ("video_quant", "video_gemm", "full_rht"):
+        elif args.only in ("video_quant", "video_gemm", "full_rht", "w8a16", "w4a16",
+                           "w8a16_narrow", "w4a16_narrow"):
             step = other_kernel(rbp, torch, dev, args.only)
         else:
             quant(pool[0])

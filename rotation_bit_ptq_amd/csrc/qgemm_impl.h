@@ -687,7 +687,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
     }
   } else {
     // KIND 2.  Chunks of 64 k; chunk c lives in LDS stage c % 3 while the
-    // loads of chunks c + 1 and c + 2 are in flight.  Loads go global -> LDS
+    // loads of chunks c + 1 and c + 2 are in flight, and its stage takes
+    // chunk c + 3 once every wave has read it.  Loads go global -> LDS
     // directly (16 bytes per lane, written in lane order), so data in flight
     // holds no registers.  Per lane and sub-step s the MFMA k order is
     //   k = 32 half + 8 s + 0..7
@@ -805,78 +806,126 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < WN; ++j) s_par[j] = (nrow[j] * (uint32_t)g.groups_per_row) & 1u;
 
+    // Operands in flight: token blocks and decoded weight blocks of two
+    // sub-steps (sub-step s of a chunk uses set s & 1), raw weights of the
+    // chunk (int8: unit r holds sub-steps 2r and 2r + 1; int4: unit 0 holds
+    // all four) and the group scales of the chunk.
+    half8 av[2][WM], bv[2][WN];
+    u32x4 braw[2][WN];
     uint32_t sc[WN];
-    u32x4 braw[WN];  // int8: two sub-steps; int4: four
-    half8 a0[WM], a1[WM];
-    // sub-step s of the chunk in stage st on token operands a, whose next
-    // sub-step's token operands are read into an meanwhile; the weight
-    // operand of block j + 1 is decoded while block j's MFMAs run
-    auto substep = [&](auto s_, const char* st, const half8 (&a)[WM], half8 (&an)[WM]) {
-      constexpr int s = decltype(s_)::value;
-      if (kI4 ? s == 0 : (s & 1) == 0) {
+    auto read_a = [&](int set, const char* st, int s) {
 #pragma unroll
-        for (int j = 0; j < WN; ++j) braw[j] = *(const u32x4*)(st + b_off[s >> 1] + j * kBBlock);
-      }
-      if constexpr (s < 3) {
-#pragma unroll
-        for (int i = 0; i < WM; ++i) an[i] = *(const half8*)(st + a_off[s + 1] + i * 4096);
-      }
-#pragma unroll
-      for (int j = 0; j < WN; ++j) {
-        OpB op;
-        if constexpr (kI4) op.v = make_uint2(braw[j][s], 0u);
-        else op.v = braw[j];
-        op.scale2 = sc[j];
-        const half8 bv = op.decode(kI4 ? 0 : (s & 1), 0);
-#pragma unroll
-        for (int i = 0; i < WM; ++i)
-          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bv, a[i], acc[j][i], 0, 0, 0);
-      }
-      // reads first, then the first decode, then one MFMA per one or two
-      // decode instructions
-      __builtin_amdgcn_sched_group_barrier(0x100, (kI4 ? s == 0 : (s & 1) == 0) ? WN + WM : WM, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 14, 0);
-#pragma unroll
-      for (int q = 0; q < WM * WN; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < WM; ++i) av[set][i] = *(const half8*)(st + a_off[s] + i * 4096);
     };
-
-    // Every chunk issues the same kLoads loads into stage (c + 2) % 3 (chunk
-    // c + 2, or a re-read of the last chunk that nobody reads again), so
-    // waiting until at most kLoads are in flight completes chunk c + 1.  The
-    // wait also drains this wave's LDS reads (lgkmcnt 0), and the empty asm
-    // statements keep the compiler from moving memory accesses across the
-    // barrier.
-    auto sync = [&]() {
-      __builtin_amdgcn_s_waitcnt(vm_wait<kLoads>() & ~(15 << 8));
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
+    auto read_raw = [&](int unit, const char* st) {
+#pragma unroll
+      for (int j = 0; j < WN; ++j) braw[unit][j] = *(const u32x4*)(st + b_off[unit] + j * kBBlock);
     };
-    issue(0, 0);
-    issue(1, 1);
-    sync();
-    for (int c = 0; c < nch; ++c) {
-      // chunk c is complete in stage c % 3 for every thread, and every wave
-      // is done reading stage (c + 2) % 3 (chunk c - 1)
-      issue(c + 2, c + 2);
-      const char* const st = smem + (c % 3) * kStage;
+    auto read_scale = [&](const char* st, int c) {
 #pragma unroll
       for (int j = 0; j < WN; ++j) {
         const uint32_t dw = *(const uint32_t*)(st + s_off + j * 128);
         const uint32_t h16 = (dw >> (16 * ((s_par[j] + (uint32_t)(c >> 1)) & 1u))) & 0xffffu;
         sc[j] = h16 | (h16 << 16);
       }
+    };
+    auto decode = [&](int set, int s) {
 #pragma unroll
-      for (int i = 0; i < WM; ++i) a0[i] = *(const half8*)(st + a_off[0] + i * 4096);
-      substep(std::integral_constant<int, 0>{}, st, a0, a1);
-      substep(std::integral_constant<int, 1>{}, st, a1, a0);
-      substep(std::integral_constant<int, 2>{}, st, a0, a1);
-      substep(std::integral_constant<int, 3>{}, st, a1, a0);
-      sync();  // chunk c + 1 complete; this chunk's LDS reads are done
+      for (int j = 0; j < WN; ++j) {
+        OpB op;
+        if constexpr (kI4) op.v = make_uint2(braw[0][j][s], 0u);
+        else op.v = braw[s >> 1][j];
+        op.scale2 = sc[j];
+        bv[set][j] = op.decode(kI4 ? 0 : (s & 1), 0);
+      }
+    };
+    auto mma = [&](int set) {
+#pragma unroll
+      for (int j = 0; j < WN; ++j)
+#pragma unroll
+        for (int i = 0; i < WM; ++i)
+          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bv[set][j], av[set][i], acc[j][i], 0, 0, 0);
+    };
+    // Issue order of a sub-step: each MFMA followed by up to R LDS reads and
+    // V VALU instructions, so the reads and the decode of the next sub-step
+    // go out while the matrix pipe works on this one.
+    auto interleave = [&](auto r_, auto v_) {
+      constexpr int R = decltype(r_)::value, V = decltype(v_)::value;
+#pragma unroll
+      for (int q = 0; q < WM * WN; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if constexpr (R > 0) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+        if constexpr (V > 0) __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    constexpr int kV = kI4 ? 3 : 2;  // decode VALU per MFMA slot
+
+    // Chunk c + 1 must be complete before the last sub-step of chunk c reads
+    // it: every chunk issues the same kLoads loads, and chunk c + 2's are the
+    // only ones issued after chunk c + 1's, so waiting until at most kLoads
+    // are in flight completes it.  The wait also drains this wave's LDS reads
+    // (lgkmcnt 0), after which the barrier means every wave is done reading
+    // chunk c's stage, which then takes chunk c + 3.  The empty asm
+    // statements keep the compiler from moving memory accesses across the
+    // barrier.
+    auto sync = [&](auto n_) {
+      __builtin_amdgcn_s_waitcnt(vm_wait<decltype(n_)::value>() & ~(15 << 8));
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+    issue(0, 0);
+    issue(1, 1);
+    issue(2, 2);
+    sync(std::integral_constant<int, 2 * kLoads>{});  // chunk 0 complete
+    read_scale(smem, 0);
+    read_raw(0, smem);
+    read_a(0, smem, 0);
+    decode(0, 0);
+    // sub-steps 0-2 of chunk c: MFMAs on set s & 1 while the token blocks of
+    // sub-step s + 1 are read and its weight blocks decoded (int8: the raw
+    // unit of sub-steps 2 and 3 is read during sub-step 0)
+    auto first3 = [&](const char* st) {
+      mma(0);
+      if constexpr (!kI4) read_raw(1, st);
+      read_a(1, st, 1);
+      decode(1, 1);
+      interleave(std::integral_constant<int, 1>{}, std::integral_constant<int, kV>{});
+      mma(1);
+      read_a(0, st, 2);
+      decode(0, 2);
+      interleave(std::integral_constant<int, 1>{}, std::integral_constant<int, kV>{});
+      mma(0);
+      read_a(1, st, 3);
+      decode(1, 3);
+      interleave(std::integral_constant<int, 1>{}, std::integral_constant<int, kV>{});
+    };
+    // The last chunk runs the same body: its reads of "chunk last + 1" read
+    // a stage that holds a re-read of the last chunk (valid LDS, values
+    // unused), so the loop has one body and no tail.
+    for (int c = 0; c < nch; ++c) {
+      const char* const st = smem + (c % 3) * kStage;
+      const char* const sn = smem + ((c + 1) % 3) * kStage;
+      first3(st);
+      // sub-step 3: chunk c + 1 complete and chunk c's stage free; its loads
+      // go out, chunk c + 1's scales, first raw unit and first token blocks
+      // are read, and its first weight blocks are decoded in the second half
+      // of the MFMAs
+      sync(std::integral_constant<int, kLoads>{});
+      issue(c + 3, c + 3);
+      read_scale(sn, c + 1);
+      read_raw(0, sn);
+      read_a(0, sn, 0);
+      mma(1);
+      decode(0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * WN + WM, 0);
+#pragma unroll
+      for (int q = 0; q < WM * WN; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (q >= WM * WN / 2) __builtin_amdgcn_sched_group_barrier(0x002, 2 * kV + 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     // the trailing re-reads must land before the epilogue reuses the ring
     __builtin_amdgcn_s_waitcnt(vm_wait<0>());
