@@ -125,6 +125,151 @@ __global__ __launch_bounds__(512) void narrow_kernel(GemmArgs g) {
   }
 }
 
+// Batches of at most 16 tokens with 8 G scale groups per row (G <= 4):
+// the weight stream is the whole cost, so the kernel is laid out for memory
+// parallelism at low register cost.  One workgroup of eight waves per
+// compute unit; wave w owns the G groups G w .. G w + G - 1 of every row and
+// keeps the tokens of those groups in registers for the whole launch.  The workgroup walks 16-row weight slabs
+// blockIdx.x, blockIdx.x + gridDim.x, ..., with the weights of three slabs
+// in flight per wave, multiplying each with v_mfma_f32_16x16x32_f16 (the
+// weights as the 16-row operand, the tokens as the 16-column operand, so no
+// token row is loaded twice).  Per group and lane: 32 k of one weight row
+// (32 bytes of int8 or 16 of int4) and 32 k of one token row (64 bytes),
+// k = 128 group + 32 (lane / 16) + 8 s + j for MFMA s = 0..3 and j < 8 on
+// both operands.  Each wave's partial sums of a slab go to LDS; after the
+// walk, wave w adds the eight partials of slabs w, w + 8, ... and writes
+// them.  Tokens past M re-read token M - 1 and weight rows past N re-read
+// row N - 1; neither is written.
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+template <class OpB, int G>
+__global__ __launch_bounds__(512) void narrow16_kernel(GemmArgs g, int slabs_per_block) {
+  constexpr int WV = 8, P = 3;
+  constexpr bool kI4 = OpB::kCodeBits == 4;
+  constexpr int kWVec = kI4 ? 1 : 2;                 // 16-byte weight loads per lane and group
+  constexpr uint32_t kGroupBytes = kI4 ? 64u : 128u;  // weight bytes of one row and group
+  extern __shared__ __align__(16) char smem[];
+  floatx4* const red = (floatx4*)smem;  // [slab of the block][wave][lane]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, kq = lane >> 4;
+  const long long slabs = (g.N + 15) / 16;
+  const int g0 = wave * G;
+
+  u32x4 tk[G][4];
+  {
+    const long long m = r16 < g.M ? r16 : g.M - 1;
+    const uint8_t* src = g.a + m * g.lda + (uint32_t)kq * 64u;
+#pragma unroll
+    for (int q = 0; q < G; ++q)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) tk[q][v] = *(const u32x4*)(src + (uint32_t)(g0 + q) * 256u + 16u * v);
+  }
+  u32x4 wt[P][G][kWVec];
+  uint32_t sc[P][G];
+  auto slab_of = [&](int i) { return (long long)blockIdx.x + (long long)i * gridDim.x; };
+  auto load = [&](int slot, int i) {
+    const long long n0 = slab_of(i) * 16 + r16;
+    const long long n = n0 < g.N ? n0 : g.N - 1;
+    const uint8_t* src = g.b + n * g.ldb + (uint32_t)kq * (kGroupBytes / 4u);
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+#pragma unroll
+      for (int v = 0; v < kWVec; ++v) wt[slot][q][v] = *(const u32x4*)(src + (uint32_t)(g0 + q) * kGroupBytes + 16u * v);
+      const uint32_t s16 = g.scale_f16[n * g.groups_per_row + g0 + q];
+      sc[slot][q] = s16 | (s16 << 16);
+    }
+  };
+  auto compute = [&](int slot) {
+    floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int q = 0; q < G; ++q)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        OpB op;
+        op.scale2 = sc[slot][q];
+        half8 bv;
+        if constexpr (kI4) {
+          op.v = make_uint2(wt[slot][q][0][s], 0u);
+          bv = op.decode(0, 0);
+        } else {
+          op.v = wt[slot][q][s >> 1];
+          bv = op.decode(s & 1, 0);
+        }
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(bv, __builtin_bit_cast(half8, tk[q][s]), acc, 0, 0, 0);
+      }
+    return acc;
+  };
+  // Slab i of the block is valid while blockIdx.x + i gridDim.x < slabs
+  // (the same for every wave); invalid slabs are neither loaded nor
+  // computed.
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+    if (slab_of(p) < slabs) load(p, p);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int i0 = 0; i0 < slabs_per_block; i0 += P) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int i = i0 + p;
+      if (i < slabs_per_block && slab_of(i) < slabs) {
+        red[(i * WV + wave) * 64 + lane] = compute(p);
+        if (slab_of(i + P) < slabs) load(p, i + P);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  __syncthreads();
+  // lane l holds weight rows 16 slab + 4 (l / 16) + 0..3 of token l % 16
+  const bool f32_out = g.out_dtype != ORBIT_BF16;
+  for (int i = wave; i < slabs_per_block && slab_of(i) < slabs; i += WV) {
+    floatx4 y = red[(i * WV) * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < WV; ++w) y += red[(i * WV + w) * 64 + lane];
+    const long long m = r16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const long long n = slab_of(i) * 16 + 4 * kq + r;
+      if (m < g.M && n < g.N) {
+        const float v = y[r] + load_bias(g, n);
+        if (f32_out) ((float*)g.out)[m * g.N + n] = v;
+        else ((uint16_t*)g.out)[m * g.N + n] = f32_to_bf16_rne(v);
+      }
+    }
+  }
+}
+
+// Up to 16 tokens and 8, 16, 24 or 32 groups per row: the slab-walking
+// kernel, one workgroup per compute unit (more when a workgroup would own
+// more than eight slabs, which bounds its LDS to 64 KB).
+template <class OpB>
+hipError_t launch_narrow16(GemmArgs& g, hipStream_t stream) {
+  DeviceInfo di;
+  hipError_t e = device_info(&di);
+  if (e != hipSuccess) return e;
+  const long long slabs = (g.N + 15) / 16;
+  long long blocks = slabs < di.n_cu ? slabs : di.n_cu;
+  if ((slabs + blocks - 1) / blocks > 8) blocks = (slabs + 7) / 8;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  const int per = (int)((slabs + blocks - 1) / blocks);
+  const size_t lds = (size_t)per * 8 * 64 * 16;
+  switch (g.groups_per_row) {
+    case 8:
+      hipLaunchKernelGGL((narrow16_kernel<OpB, 1>), dim3((unsigned)blocks), dim3(512), lds, stream, g, per);
+      break;
+    case 16:
+      hipLaunchKernelGGL((narrow16_kernel<OpB, 2>), dim3((unsigned)blocks), dim3(512), lds, stream, g, per);
+      break;
+    case 24:
+      hipLaunchKernelGGL((narrow16_kernel<OpB, 3>), dim3((unsigned)blocks), dim3(512), lds, stream, g, per);
+      break;
+    case 32:
+      hipLaunchKernelGGL((narrow16_kernel<OpB, 4>), dim3((unsigned)blocks), dim3(512), lds, stream, g, per);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 // Eight waves split K when it holds a multiple of eight groups, four when a
 // multiple of four, else one.
 template <class OpB, int MB>
@@ -148,6 +293,7 @@ hipError_t launch_narrow(GemmArgs& g, hipStream_t stream) {
 // dword would reach past the array).
 template <class OpB>
 hipError_t launch_weight_only(GemmArgs& g, hipStream_t stream) {
+  if (g.M <= 16 && g.groups_per_row % 8 == 0 && g.groups_per_row <= 32) return launch_narrow16<OpB>(g, stream);
   if (g.M <= 32) return launch_narrow<OpB, 1>(g, stream);
   const long long tiles = ((g.M + 255) / 256) * ((g.N + 255) / 256);
   const bool scales_ok = ((uintptr_t)g.scale_f16 & 3) == 0 && (g.N * g.groups_per_row) % 2 == 0;

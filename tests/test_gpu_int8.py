@@ -120,8 +120,14 @@ def test_int8_linear_ragged(gpu_lib, M, N):
 STAGED = [(4096, 2048, 512), (4000, 2100, 256), (4096, 2048, 128), (4096, 2049, 384),
           (4096, 2048, 4096),   # the int8 workload's K
 
-          # narrow batches (M <= 32: one workgroup per 32 weight rows; 64: small tiles)
-          (16, 4608, 3072), (64, 1000, 1024), (5, 33, 128)]
+          # narrow batches (up to 32 tokens: one workgroup per 32 weight rows; 64:
+          # small tiles)
+          (24, 600, 3072), (64, 1000, 1024), (5, 33, 128),
+          # up to 16 tokens and 8, 16, 24 or 32 groups per row: one workgroup per
+          # compute unit walking 16-row slabs (the AdaLN-style projection at full
+          # size; a single slab; more than 2048 slabs, eight per workgroup)
+          (16, 18432, 3072), (16, 4608, 3072), (1, 100, 1024), (7, 1000, 2048),
+          (16, 4100, 4096), (12, 16, 3072), (3, 40000, 1024)]
 
 
 @pytest.mark.parametrize("M,N,K", STAGED)
