@@ -229,21 +229,27 @@ def weight_only(rbp, torch, dev, stream, n=10):
     on two shapes: the int8 workload (16384 tokens, 4096 -> 4096, h = 128;
     compute-bound) and an AdaLN-style projection (16 conditioning vectors,
     3072 -> 18432; bound by the weight stream).  Per shape: the rotation of
-    the activations (bf16 -> fp16) and each GEMM in microseconds per launch,
-    with TFLOP/s and the weight bytes streamed per microsecond (GB/s)."""
+    the activations (bf16 -> fp16) and each GEMM in microseconds per launch
+    (the same weights every launch), with TFLOP/s and the weight bytes
+    streamed per microsecond (GB/s)."""
     import synth
 
     def timed(fn):
-        for _ in range(2):
+        # the median of three runs of n back-to-back launches after five
+        # warm-up launches (the clock settles over the first few)
+        for _ in range(5):
             fn()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(n):
-            fn()
-        b.record(stream)
-        b.synchronize()
-        return a.elapsed_time(b) * 1e3 / n
+        runs = []
+        for _ in range(3):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(n):
+                fn()
+            b.record(stream)
+            b.synchronize()
+            runs.append(a.elapsed_time(b) * 1e3 / n)
+        return sorted(runs)[1]
 
     res = {}
     for name, (M, K, N) in (("int8_workload_16384x4096x4096", (16384, 4096, 4096)),

@@ -155,14 +155,16 @@ def test_layer_full_size_sampled(gpu_lib, label, cfg, ba, bw):
 
 
 @pytest.mark.parametrize("cfg,ba,bw,M,N,TN", [(5, 6, 4, 4608, 8192 + 96, 384),
-                                               (5, 6, 4, 6144, 8192 + 96, 512),
+                                               (5, 6, 4, 6144, 8192 + 96, 256),
+                                               (5, 6, 4, 4096, 12032, 512),
                                                (4, 4, 2, 12800, 4096 + 40, 512)])
 def test_wide_tile_ragged(gpu_lib, cfg, ba, bw, M, N, TN):
-    """Products with enough tiles to take the wide wave tiles: 2 x 6 (128 x
-    384 per workgroup) or 2 x 8 (128 x 512) for 6-bit tokens, 2 x 8 for
-    2-bit weights; each with a ragged last column of tiles.  Sampled tokens
-    against every output column of the last two tile columns and sampled
-    ones elsewhere."""
+    """Products with enough tiles to take the wide wave tiles, for 6-bit
+    tokens and 4-bit weights: 2 x 6 (128 x 384 per workgroup), 4 x 4 (256 x
+    256) and 2 x 8 (128 x 512, where a ragged last column gives 752 tiles of
+    256 x 256 and 768 of 128 x 512); 2 x 8 for 2-bit weights; each with a
+    ragged last column of tiles.  Sampled tokens against every output
+    column of the last two tile columns and sampled ones elsewhere."""
     rbp = gpu_lib
     inp = synth.make(cfg, M=M, N=N)
     K = inp["K"]
