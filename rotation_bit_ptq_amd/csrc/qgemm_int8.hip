@@ -6,8 +6,9 @@ namespace orbit {
 namespace qgemm {
 namespace {
 
-// Narrow batches (M <= 32 tokens, e.g. conditioning vectors): the product is
-// bound by the weight stream.  Each workgroup owns 32 weight rows and all
+// Narrow batches (M <= 32 tokens, e.g. conditioning vectors, where the
+// slab-walking kernel below does not apply): the product is bound by the
+// weight stream.  Each workgroup owns 32 weight rows and all
 // tokens; its WV waves split K in groups of 128 (one scale group), reduced
 // in LDS.  Per group a lane reads whole cache lines: 64 (int8) or 32 (int4)
 // contiguous bytes of its weight row (the two halves of a row are adjacent)
@@ -285,9 +286,10 @@ hipError_t launch_narrow(GemmArgs& g, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Narrow batches (up to 32 tokens) take the narrow kernel; large products
-// the LDS-staged kernel (256 x 256 tiles, a ring of three 64-k chunks); the
-// rest the register-fed kernel and its smaller tiles.  The staged kernel reads each
+// Up to 16 tokens with 8, 16, 24 or 32 groups per row take the slab-walking
+// kernel, other batches of up to 32 tokens the 32-row narrow kernel; large
+// products the LDS-staged kernel (256 x 256 tiles, a ring of three 64-k
+// chunks); the rest the register-fed kernel and its smaller tiles.  The staged kernel reads each
 // fp16 group scale through the aligned dword that holds it, so it also needs
 // a 4-byte aligned scale array with an even number of entries (else the last
 // dword would reach past the array).
