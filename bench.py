@@ -130,6 +130,25 @@ def cpu_baseline(inp, gpu_idx, gpu_s, rounds_target_s=10.0, block=512):
         "s_max_rel_err": s_err}
 
 
+def settled_launch_us(torch, stream, fn, n, warmup=5, runs=3):
+    """Microseconds per launch of fn on the launching stream: the median of
+    `runs` runs of n back-to-back launches (events around each run) after
+    `warmup` launches, over which the clock settles."""
+    for _ in range(warmup):
+        fn()
+    per = []
+    for _ in range(runs):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        b.synchronize()
+        per.append(a.elapsed_time(b) * 1e3 / n)
+    return sorted(per)[len(per) // 2]
+
+
 def rotation_ablation(rbp, torch, dev, stream, M=16384, d=4096, h=128, n=20):
     """The rotation variants of OrbitQuant's ablation (page, Experiments) on
     the 16384 x 4096 bf16 activations of the int8 workload (d a power of two,
@@ -148,16 +167,7 @@ def rotation_ablation(rbp, torch, dev, stream, M=16384, d=4096, h=128, n=20):
             "full_rht_h4096": rbp.Rotation(perm, signs, d)}
 
     def timed(fn):
-        for _ in range(3):
-            fn()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(n):
-            fn()
-        b.record(stream)
-        b.synchronize()
-        return a.elapsed_time(b) * 1e3 / n
+        return settled_launch_us(torch, stream, fn, n)
 
     res = {k: round(timed(lambda r=r: rbp.rotate(r, X, out_dtype=torch.float16, out=out)), 2)
            for k, r in rots.items()}
@@ -207,15 +217,7 @@ def mlp_pair(rbp, torch, dev, stream, n=3):
         rbp.qlinear(ib, s2, ca_dn, iw_dn, r_dn, cw_dn, N, out=out)
 
     def timed(fn):
-        fn()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(n):
-            fn()
-        b.record(stream)
-        b.synchronize()
-        return a.elapsed_time(b) * 1e3 / n
+        return settled_launch_us(torch, stream, fn, n)
 
     tf, tu = timed(fused), timed(unfused)
     flops = 2.0 * 2 * M * K * N
@@ -235,21 +237,7 @@ def weight_only(rbp, torch, dev, stream, n=10):
     import synth
 
     def timed(fn):
-        # the median of three runs of n back-to-back launches after five
-        # warm-up launches (the clock settles over the first few)
-        for _ in range(5):
-            fn()
-        runs = []
-        for _ in range(3):
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for _ in range(n):
-                fn()
-            b.record(stream)
-            b.synchronize()
-            runs.append(a.elapsed_time(b) * 1e3 / n)
-        return sorted(runs)[1]
+        return settled_launch_us(torch, stream, fn, n)
 
     res = {}
     for name, (M, K, N) in (("int8_workload_16384x4096x4096", (16384, 4096, 4096)),
@@ -293,16 +281,7 @@ def video_layer(rbp, torch, dev, stream, n=10):
     out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
 
     def timed(fn):
-        for _ in range(2):
-            fn()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(n):
-            fn()
-        b.record(stream)
-        b.synchronize()
-        return a.elapsed_time(b) * 1e3 / n
+        return settled_launch_us(torch, stream, fn, n)
 
     tq = timed(lambda: rbp.quant_act(rot, ca, X))
     tg = timed(lambda: rbp.qlinear(ia, s, ca, iw, r, cw, K, out=out))
