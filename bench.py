@@ -430,11 +430,13 @@ def quant_neighbours(torch, dev, stream, quant, gemm, pool, n=40):
             "after_copy_25MiB": timed(lambda: dst.copy_(src)), "unit": "us (median, events per launch)"}
 
 
-def measured_peaks(torch, dev, stream, trips=20000):
+def measured_peaks(torch, dev, stream, trips=20000, chains_sweep=False):
     """Ceilings measured on this device: a plain device copy (HBM read +
     write) and a loop of fp16 matrix-core products from registers (random
     normal operands, which set the clock the matrix cores run at under
-    load, and constant ones), with the shader clock over the loop."""
+    load, and constant ones), with the shader clock over the loop.  With
+    chains_sweep, also the random-operand loop with 4, 8, 12 and 16
+    independent accumulators per wave, at one and two waves per SIMD."""
     import ctypes
     res = {}
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
@@ -454,6 +456,13 @@ def measured_peaks(torch, dev, stream, trips=20000):
     sink = torch.empty(n_cu * 2 * 256, dtype=torch.float32, device=dev)
     clocks = torch.zeros(2, dtype=torch.int64, device=dev)
     sp = ctypes.c_void_p(stream.cuda_stream)
+    # warm-up: the first loops after other work run before the shader clock
+    # has settled (measured 1.46 against 1.71 PFLOP/s for the same loop run
+    # first and second), so ~40 ms of the random-operand loop go first
+    for _ in range(6):
+        assert lib.peaks_mfma_loop(ctypes.c_void_p(seeds["random"].data_ptr()), trips, 1,
+                                   ctypes.c_void_p(sink.data_ptr()),
+                                   ctypes.c_void_p(clocks.data_ptr()), sp) == 0
     for kind, seed in seeds.items():
         for wps in (1, 2):
             run = lambda i: lib.peaks_mfma_loop(ctypes.c_void_p(seed.data_ptr()), trips, wps,  # noqa: E731
@@ -465,6 +474,24 @@ def measured_peaks(torch, dev, stream, trips=20000):
             ck = clocks.cpu().numpy()
             res[f"mfma_{kind}_{wps}w_tflops"] = round(flops / st["mean_us"] / 1e6, 1)
             res[f"mfma_{kind}_{wps}w_sclk_ghz"] = round(float(ck[0]) / float(ck[1]) * wall_ghz, 3)
+    if chains_sweep:
+        lib.peaks_mfma_loop_chains.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        sweep = {}
+        for ch in (4, 8, 12, 16):
+            for wps in (1, 2):
+                tr = trips * 4 // ch  # the same products per wave
+                run = lambda i: lib.peaks_mfma_loop_chains(  # noqa: E731
+                    ctypes.c_void_p(seeds["random"].data_ptr()), tr, wps, ch,
+                    ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(clocks.data_ptr()), sp)
+                assert run(0) == 0
+                st = launch_stats(torch, stream, run, 5)
+                flops = 2.0 * 32 * 32 * 16 * ch * tr * n_cu * 4 * wps
+                ck = clocks.cpu().numpy()
+                sweep[f"{ch}_chains_{wps}w"] = {
+                    "tflops": round(flops / st["mean_us"] / 1e6, 1),
+                    "sclk_ghz": round(float(ck[0]) / float(ck[1]) * wall_ghz, 3)}
+        res["mfma_random_chains"] = sweep
     # LDS reads per compute unit and shader clock (eight waves, independent
     # reads, no bank conflicts): 4-byte lanes as a decode lookup, 16-byte
     # lanes as an MFMA operand
@@ -532,7 +559,8 @@ def main():
     if args.only is not None:
         # one kernel alone, for rocprofv3 counter passes (no timing line)
         if args.only == "mfma":
-            print(json.dumps({"only": "mfma", **measured_peaks(torch, dev, stream)}), flush=True)
+            print(json.dumps({"only": "mfma", **measured_peaks(torch, dev, stream, chains_sweep=True)}),
+                  flush=True)
             return
         if args.only == "copy":
             src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)

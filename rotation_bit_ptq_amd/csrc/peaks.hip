@@ -18,9 +18,11 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 // before it.  Operands come from `seed` (random normal fp16 values give the
 // matrix cores' real power draw; constant ones do not).  clocks[0..1] of
 // the first wave: shader clock ticks and 100 MHz wall-clock ticks over the
-// loop.
+// loop.  The ceilings use 4 chains; 8, 12 and 16 show that more
+// independent work per wave does not change the rate.
 constexpr int kChains = 4;
 
+template <int kChains>
 __global__ __launch_bounds__(256) void mfma_loop_kernel(const uint4* seed, int trips,
                                                         float* sink, long long* clocks) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
@@ -118,12 +120,32 @@ int peaks_mfma_loop(const void* seed, int trips, int waves_per_simd, float* sink
   if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return (int)e;
   if (trips < 1 || waves_per_simd < 1 || waves_per_simd > 2) return (int)hipErrorInvalidValue;
-  hipLaunchKernelGGL(mfma_loop_kernel, dim3(n_cu * waves_per_simd), dim3(256), 0, stream,
+  hipLaunchKernelGGL(mfma_loop_kernel<kChains>, dim3(n_cu * waves_per_simd), dim3(256), 0, stream,
                      (const uint4*)seed, trips, sink, clocks);
   return (int)hipGetLastError();
 }
 
 int peaks_mfma_chains(void) { return kChains; }
+
+// The same loop with `chains` (4, 8, 12 or 16) accumulators per wave.
+// flops per launch = 2 * 32 * 32 * 16 * chains * trips * waves.
+int peaks_mfma_loop_chains(const void* seed, int trips, int waves_per_simd, int chains,
+                           float* sink, long long* clocks, hipStream_t stream) {
+  int dev = 0, n_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return (int)e;
+  if (trips < 1 || waves_per_simd < 1 || waves_per_simd > 2) return (int)hipErrorInvalidValue;
+  const dim3 grid(n_cu * waves_per_simd), block(256);
+  switch (chains) {
+    case 4: hipLaunchKernelGGL(mfma_loop_kernel<4>, grid, block, 0, stream, (const uint4*)seed, trips, sink, clocks); break;
+    case 8: hipLaunchKernelGGL(mfma_loop_kernel<8>, grid, block, 0, stream, (const uint4*)seed, trips, sink, clocks); break;
+    case 12: hipLaunchKernelGGL(mfma_loop_kernel<12>, grid, block, 0, stream, (const uint4*)seed, trips, sink, clocks); break;
+    case 16: hipLaunchKernelGGL(mfma_loop_kernel<16>, grid, block, 0, stream, (const uint4*)seed, trips, sink, clocks); break;
+    default: return (int)hipErrorInvalidValue;
+  }
+  return (int)hipGetLastError();
+}
 
 // Rate of the wall clock read by the loop, in kHz (0 on error).
 int peaks_wall_clock_khz(void) {
