@@ -43,14 +43,14 @@ def parse():
                     help="per-launch HBM bytes measured with rocprofv3 counters")
     ap.add_argument("--only", choices=["quant", "gemm", "copy", "mfma", "video_quant",
                                        "video_gemm", "full_rht", "w8a16", "w4a16",
-                                       "w8a16_narrow", "w4a16_narrow"], default=None,
+                                       "w8a16_narrow", "w4a16_narrow", "mlp_up_gemm"], default=None,
                     help="launch only one kernel --steps times (for counter runs): the "
                          "activation rotate+quantize, the decode GEMM, a plain device "
                          "copy of COPY_BYTES that calibrates FETCH_SIZE / WRITE_SIZE, "
                          "the matrix-core loop of the measured MFMA ceiling, the video "
                          "projection's quantizer or GEMM, the full RHT (h = d = 4096) "
-                         "of the rotation ablation, or a weight-only GEMM (int8 workload, "
-                         "or the AdaLN-style shape with _narrow)")
+                         "of the rotation ablation, a weight-only GEMM (int8 workload, "
+                         "or the AdaLN-style shape with _narrow), or the MLP pair's up GEMM")
     return ap.parse_args()
 
 
@@ -293,12 +293,22 @@ def video_layer(rbp, torch, dev, stream, n=10):
 
 def other_kernel(rbp, torch, dev, which):
     """One launch of the video projection's quantizer or GEMM, of the full
-    RHT of the rotation ablation, or of a weight-only GEMM (the int8
+    RHT of the rotation ablation, of a weight-only GEMM (the int8
     workload's 16384 x 4096 -> 4096, or the AdaLN-style 16 x 3072 -> 18432
-    with _narrow), as a function of the step, for the counter passes of
+    with _narrow), or of the MLP pair's up GEMM (16384 x 3072 -> 12288,
+    W2A4, GELU), as a function of the step, for the counter passes of
     --only."""
     import synth
     to = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    if which == "mlp_up_gemm":
+        inp = synth.make(4)
+        M, K, N = inp["M"], inp["K"], inp["N"]
+        rot = rbp.Rotation(inp["perm"], inp["signs"], 256)
+        ca, cw = rbp.Codebook(K, 4), rbp.Codebook(K, 2)
+        iw, r = rbp.pack_weights(rot, cw, to(inp["W"]))
+        ia, s = rbp.quant_act(rot, ca, to(inp["X"]))
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        return lambda i: rbp.qlinear(ia, s, ca, iw, r, cw, K, out=out, act="gelu")
     if which.startswith(("w8a16", "w4a16")):
         M, K, N = (16, 3072, 18432) if which.endswith("_narrow") else (16384, 4096, 4096)
         perm, signs = synth.rotation_params(K, 7)
@@ -569,7 +579,7 @@ def main():
         elif args.only == "quant":
             step = lambda i: quant(pool[i % pool_n])  # noqa: E731
         elif args.only in ("video_quant", "video_gemm", "full_rht", "w8a16", "w4a16",
-                           "w8a16_narrow", "w4a16_narrow"):
+                           "w8a16_narrow", "w4a16_narrow", "mlp_up_gemm"):
             step = other_kernel(rbp, torch, dev, args.only)
         else:
             quant(pool[0])
