@@ -147,6 +147,30 @@ def test_int8_linear_staged_tiles(gpu_lib, M, N, K):
     assert rel_fro(out_f64(out16), y) < OUT_TOL
 
 
+@pytest.mark.parametrize("M,N,K", [(16, 1000, 2048), (9, 37, 4096), (3, 40000, 1024)])
+def test_int8_narrow_bf16_bias_deterministic(gpu_lib, M, N, K):
+    """The slab-walking kernel (up to 16 tokens) with a bf16 bias, into both
+    output types, against the exact product on the GPU's own fp16 x' plus the
+    bias's bf16 value; two launches give identical bits (the eight waves'
+    partials are added in a fixed order)."""
+    from oracle.int8 import int8_linear_rotated
+    rbp = gpu_lib
+    inp = synth.make(3, M=M, N=N, K=K, h=128)
+    rot = rbp.Rotation(inp["perm"], inp["signs"], 128)
+    q, sc = rbp.int8_pack_weights(rot, to_dev(inp["W"]), 128)
+    xr = rbp.rotate(rot, to_dev(inp["X"]), torch.float16)
+    b32 = np.random.default_rng(4).standard_normal(N).astype(np.float32)
+    bias = torch.from_numpy(b32).cuda().to(torch.bfloat16)
+    bias_f64 = bias.float().cpu().numpy().astype(np.float64)
+    y = int8_linear_rotated(oracle.f16_bits_to_f64(bits_of(xr)), q.cpu().numpy(), bits_of(sc), 128) + bias_f64
+    out32 = rbp.int8_linear(xr, q, sc, 128, bias=bias, out_dtype=torch.float32)
+    assert rel_fro(out_f64(out32), y) < 2.0 ** -11
+    out16 = rbp.int8_linear(xr, q, sc, 128, bias=bias)
+    assert rel_fro(out_f64(out16), y) < OUT_TOL
+    again = rbp.int8_linear(xr, q, sc, 128, bias=bias)
+    assert torch.equal(out16, again)
+
+
 def test_int8_workload_full_size_sampled(gpu_lib):
     """The int8 workload at its full size (16384 tokens, 4096 -> 4096, h = 128)
     in the launch the benchmark times: sampled outputs against the literal
