@@ -116,8 +116,9 @@ orbit_status orbit_last_hip_error(int *hip_error_out);
 /* Length in uint16 entries of the gather plan of a rotation of dimension d
  * and block h: 1024 per round of 1024 coordinates, at least 4096
  * (L = 1024 * max(4, ceil(d / 1024))), plus d entries of matrix-core words
- * when h is 64 .. 4096 and d is a multiple of 512 (d <= 16384); 0 for
- * invalid d, h.  Host only. */
+ * when h is 64 .. 4096 and d is a multiple of 512 (d <= 16384), plus d
+ * entries of the scatter section when h is 128 or 256 and d is 1024, 2048,
+ * 3072, 4096, 8192, 12288 or 16384; 0 for invalid d, h.  Host only. */
 int64_t orbit_rpbh_gather_len(int32_t d, int32_t h);
 
 /* Builds the gather plan of `rot` (its `gather` field is ignored) into the
@@ -144,8 +145,14 @@ int64_t orbit_rpbh_gather_len(int32_t d, int32_t h);
  * 1024 floor(o / 2) + 256 floor(r16 / 4) + 64 kq + 8 j + 4 (o mod 2) +
  * (r16 mod 4) for h = 256; off(k) = 2 p + 16 floor(p / 64) with p = perm[k]
  * when d <= 12288 (a 16-byte pad after every 64 coordinates), 2 p beyond.
- * Errors: ORBIT_E_ARG (null or misaligned pointers), ORBIT_E_SHAPE (d, h),
- * ORBIT_E_HIP. */
+ * The scatter section (when present) follows the words: d uint16 entries,
+ * entry perm[k] = off'(k) | (D_k = -1) << 15, off'(k) = 16 (64 o + l) + 2 j
+ * for the slot (o, l, j) of the h = 128 / 256 order above that holds
+ * coordinate k: the LDS byte offset at which the activation quantizer's
+ * lanes write x[perm[k]], sign-flipped, so that each lane's operand is 16
+ * contiguous bytes.
+ * Errors: ORBIT_E_ARG (null or misaligned pointers, or perm not a
+ * permutation of 0 .. d-1), ORBIT_E_SHAPE (d, h), ORBIT_E_HIP. */
 orbit_status orbit_rpbh_build_gather(orbit_rpbh *rot, uint16_t *out, hipStream_t stream);
 
 /* Fit the Lloyd-Max codebook for N(0,1) with 2^bits levels, in fp64, on the

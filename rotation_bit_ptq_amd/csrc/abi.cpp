@@ -226,7 +226,7 @@ orbit_status orbit_last_hip_error(int* hip_error_out) {
 int64_t orbit_rpbh_gather_len(int32_t d, int32_t h) {
   if (d < 16 || d > ORBIT_MAX_D || !pow2(h) || h < 16 || h > 4096 || d % h) return 0;
   if (h > 1024 && d > 4096) return 0;
-  return (int64_t)orbit::gather_len(d) + orbit::mfma_words_len(d, h);
+  return (int64_t)orbit::gather_len(d) + orbit::mfma_words_len(d, h) + orbit::scatter_len(d, h);
 }
 
 orbit_status orbit_rpbh_build_gather(orbit_rpbh* rot, uint16_t* out, hipStream_t stream) {
@@ -242,8 +242,16 @@ orbit_status orbit_rpbh_build_gather(orbit_rpbh* rot, uint16_t* out, hipStream_t
                                 hipMemcpyDeviceToHost, stream);
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
   if (e != hipSuccess) return hip_status(e);
+  // the plan's sections assume a permutation (the scatter section has one
+  // entry per input coordinate)
+  std::vector<char> seen((size_t)rot->d, 0);
   bool ident = true;
-  for (int32_t k = 0; k < rot->d && ident; ++k) ident = host[(size_t)k] == k;
+  for (int32_t k = 0; k < rot->d; ++k) {
+    const int32_t p = host[(size_t)k];
+    if (p < 0 || p >= rot->d || seen[(size_t)p]) return ORBIT_E_ARG;
+    seen[(size_t)p] = 1;
+    ident = ident && p == k;
+  }
   rot->flags = ident ? ORBIT_RPBH_IDENTITY : 0;
   return hip_status(orbit::launch_gather_plan(rot->d, rot->h, rot->perm, rot->sign_bits, out, stream));
 }

@@ -88,6 +88,16 @@ __host__ __device__ inline int mfma_words_len(int d, int h) {
   const bool hk = h == 64 || h == 128 || h == 256 || h == 512 || h == 1024 || h == 2048 || h == 4096;
   return (hk && d % 512 == 0 && d <= 16384) ? d : 0;
 }
+// The plan's third section, after the offset words: for the packed-code
+// matrix-core kernels (h = 128 or 256 on rows of 1024 .. 16384), one uint16
+// entry per input coordinate i holding the LDS byte offset of the operand
+// slot that needs x[i] (the slot of permuted index k = pi^-1(i)) and, in
+// bit 15, the sign flip D_k, so each lane scatters the row it loaded
+// straight into operand order.
+__host__ __device__ inline int scatter_len(int d, int h) {
+  const bool dk = d == 1024 || d == 2048 || d == 3072 || d == 4096 || d == 8192 || d == 12288 || d == 16384;
+  return ((h == 128 || (h == 256 && d % 1024 == 0)) && dk) ? d : 0;
+}
 hipError_t launch_gather_plan(int d, int h, const int32_t* perm, const uint32_t* sign_bits,
                               uint16_t* out, hipStream_t stream);
 

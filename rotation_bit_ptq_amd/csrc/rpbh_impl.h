@@ -61,6 +61,7 @@ struct RowArgs {
   const uint32_t* sign_bits;
   const uint16_t* gather;  // gather plan in this kernel's order, or null
   const uint32_t* mfma_words;  // the plan's matrix-core offset words, or null
+  const uint32_t* scatter_words;  // the plan's scatter section (two entries per word), or null
   int perm_identity;       // 1: perm[k] == k (the matrix-core kernels read rows directly)
   const void* in;
   float sqrt_d_over_h;  // sqrt(d / h): u = z * sqrt(d/h) / (s + eps), z = H y unnormalised

@@ -40,6 +40,7 @@ namespace rows {
 namespace m2 {
 
 typedef unsigned short ushort2v __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) uint16_t lds_u16_st_t;
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // The two 32 x 16 halves of H_32 as each lane's B operands (lane l = 16 kq
@@ -89,10 +90,8 @@ __host__ __device__ constexpr int slot_k(int o, int kq, int r16, int j) {
 // y_k = D_k x[pi(k)] as two bf16 in one register: the word holds the LDS
 // byte offsets of the pair in bits 0-14 and 16-30 and their sign flips in
 // bits 15 and 31.  Four VALU per pair: the two offsets, the merge and the
-// sign XOR (v_bitop3).  The empty asm keeps the words packed: unpacked
-// once outside the row loop they would take three times the registers.
+// sign XOR (v_bitop3).
 __device__ __forceinline__ uint32_t gather_pair(uint32_t w) {
-  asm volatile("" : "+v"(w));
   ushort2v p;
   p.x = *(lds_cu16_t*)(uintptr_t)(w & 0x7fffu);
   p.y = *(lds_cu16_t*)(uintptr_t)((w >> 16) & 0x7fffu);
@@ -123,6 +122,28 @@ __device__ __forceinline__ void load_words(const RowArgs& a, int o0, int lane,
       w[i][q] = row_addr<kPad>(a.perm[k0]) | (s0 << 15) | (row_addr<kPad>(a.perm[k1]) << 16) | (s1 << 31);
     }
   }
+}
+
+// Scatters one loaded dword (bf16 x[i], x[i + 1]) to the operand slots
+// that need it: the plan's scatter word holds the two slots' LDS byte
+// offsets in bits 0-14 and 16-30 and the sign flips D of their permuted
+// indices in bits 15 and 31.  Three VALU per pair (the sign XOR and the two
+// offsets); the high half goes out with ds_write_b16_d16_hi.
+__device__ __forceinline__ void scatter_pair(uint32_t x, uint32_t w) {
+  const uint32_t y = x ^ (w & 0x80008000u);
+  *(lds_u16_st_t*)(uintptr_t)(w & 0x7fffu) = (uint16_t)y;
+  *(lds_u16_st_t*)(uintptr_t)((w >> 16) & 0x7fffu) = (uint16_t)(y >> 16);
+}
+
+// Redefines the offset words at the top of every row (an empty asm, in
+// place: no copy), so the compiler cannot unpack them once outside the row
+// loop, which would take three times their registers.
+template <int N>
+__device__ __forceinline__ void opaque_words(uint32_t (&w)[N][4]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) asm volatile("" : "+v"(w[i][q]));
 }
 
 // Stores n code bytes (n = 1..8) at p from the packed value v (LSB first),
@@ -157,7 +178,7 @@ __device__ __forceinline__ void store_code_bytes(uint8_t* p, uint64_t v) {
 // (one run of 8).  The gathers of unit u + 1 are in flight during the steps
 // of unit u, and the grid-cell reads of step s while step s + 1 multiplies;
 // the codes of step s are packed and stored during step s + 1.
-template <int MODE, int BITS, int G, int NU, int D, bool kX>
+template <int MODE, int BITS, int G, int NU, int D, bool kX, bool kSc>
 __device__ __forceinline__ void units(const RowArgs& a, long long row, int u0,
                                       uint32_t (&w)[NU * Unit<G>::kOps][4],
                                       const bf16x8& hb0, const bf16x8& hb1, float cell_a,
@@ -186,9 +207,15 @@ __device__ __forceinline__ void units(const RowArgs& a, long long row, int u0,
   uint32_t pr[2][NO][4];
   auto gather = [&](int u) {
 #pragma unroll
-    for (int o = 0; o < NO; ++o)
+    for (int o = 0; o < NO; ++o) {
+      if constexpr (kSc) {  // the row was scattered into operand order
+        const u32x4 v = *(const u32x4*)(smem + 16 * (64 * (NO * (u0 + u) + o) + lane));
+        pr[u & 1][o][0] = v.x; pr[u & 1][o][1] = v.y; pr[u & 1][o][2] = v.z; pr[u & 1][o][3] = v.w;
+      } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) pr[u & 1][o][q] = gather_pair(w[NO * u + o][q]);
+        for (int q = 0; q < 4; ++q) pr[u & 1][o][q] = gather_pair(w[NO * u + o][q]);
+      }
+    }
   };
   gather(0);
   float uu[2][8];
@@ -290,7 +317,10 @@ constexpr int waves_hint(int G, int NU, int BITS, bool x) {
   return x ? 2 : ((G == 4 ? 512 : 1024) * NU <= (G == 8 || BITS == 6 ? 2048 : 3072) ? 4 : 3);
 }
 
-template <int MODE, int BITS, int G, int NU, int W, bool kX>
+// kSc: the row is scattered into operand order through the plan's scatter
+// section (a permuting rotation with a plan) and each operand is one
+// 16-byte read; otherwise the lanes gather their operands from the row.
+template <int MODE, int BITS, int G, int NU, int W, bool kX, bool kSc>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(waves_hint(G, NU, BITS, kX))))
 void kernel(RowArgs a) {
   static_assert(MODE == kAct || MODE == kWeight || MODE == kRotF16, "codebook modes and fp16 x'");
@@ -302,6 +332,7 @@ void kernel(RowArgs a) {
   constexpr int NT = 64 * W;            // threads per row
   constexpr int NCH = D / 8 / NT;       // 16-byte row chunks per thread
   static_assert(D / 8 % NT == 0, "whole chunks per thread");
+  static_assert(NCH == NU * NO, "one offset word set per 16-byte chunk or per operand");
   constexpr uint32_t kRed = (uint32_t)row_lds_bytes(D);      // four wave sums (W = 4)
   constexpr uint32_t kGrid = kRed + 16u;                      // the grid table
   extern __shared__ __align__(16) char smem[];
@@ -323,7 +354,15 @@ void kernel(RowArgs a) {
   long long row = blockIdx.x;
   load(row < a.rows ? row : a.rows - 1);
   uint32_t w[NU * NO][4];
-  load_words<G, NU * NO, kPad>(a, NO * NU * wave, lane, w);
+  if constexpr (kSc) {  // scatter words of this thread's chunks (plan order)
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const u32x4 v = *(const u32x4*)(a.scatter_words + 4 * (t + NT * i));
+      w[i][0] = v.x; w[i][1] = v.y; w[i][2] = v.z; w[i][3] = v.w;
+    }
+  } else {
+    load_words<G, NU * NO, kPad>(a, NO * NU * wave, lane, w);
+  }
   // The quantizer compares the unscaled rotated values v (u = alpha v)
   // with the row's thresholds t / alpha, rewritten in the grid each row
   // from a copy of the grid's thresholds kept after it, and the cell of v
@@ -343,12 +382,19 @@ void kernel(RowArgs a) {
   };
 
   for (; row < a.rows; row += gridDim.x) {
+    opaque_words(w);
     float ssx = 0.0f;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       if constexpr (kQuant) ssx = RowRegs<uint16_t, 1>::chunk_sumsq(pre[i], ssx);
-      const int c = t + NT * i;  // chunk c: coordinates 8 c .. 8 c + 7
-      *(u32x4*)(smem + row_addr<kPad>(8 * c)) = pre[i];
+      if constexpr (kSc) {
+        const uint32_t x[4] = {pre[i].x, pre[i].y, pre[i].z, pre[i].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) scatter_pair(x[q], w[i][q]);
+      } else {
+        const int c = t + NT * i;  // chunk c: coordinates 8 c .. 8 c + 7
+        *(u32x4*)(smem + row_addr<kPad>(8 * c)) = pre[i];
+      }
     }
     if (row + gridDim.x < a.rows) load(row + gridDim.x);
     float alpha = 0.0f;
@@ -370,12 +416,12 @@ void kernel(RowArgs a) {
         __syncthreads();  // the row's thresholds are in LDS
       }
     }
-    units<MODE, BITS, G, NU, D, kX>(a, row, NU * wave, w, hb0, hb1, alpha * a.ga, gbias, lane);
+    units<MODE, BITS, G, NU, D, kX, kSc>(a, row, NU * wave, w, hb0, hb1, alpha * a.ga, gbias, lane);
     __syncthreads();  // every lane has gathered before the next row lands
   }
 }
 
-template <int MODE, int BITS, int G, int NU, int W, bool kX>
+template <int MODE, int BITS, int G, int NU, int W, bool kX, bool kSc>
 hipError_t launch_typed(const RowArgs& a, hipStream_t stream) {
   DeviceInfo di;
   hipError_t e = device_info(&di);
@@ -384,7 +430,7 @@ hipError_t launch_typed(const RowArgs& a, hipStream_t stream) {
   // the row, four wave sums, the grid and a copy of its thresholds
   const int lds = row_lds_bytes(D) + 16 + a.grid_bytes + a.grid_bytes / 2;
   if (lds > di.max_lds) return hipErrorInvalidValue;
-  auto kern = kernel<MODE, BITS, G, NU, W, kX>;
+  auto kern = kernel<MODE, BITS, G, NU, W, kX, kSc>;
   static LaunchCache cache;
   int per_cu = 1;
   e = prepare_launch(cache, (const void*)kern, 64 * W, lds, &per_cu);
@@ -395,20 +441,30 @@ hipError_t launch_typed(const RowArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int MODE, int BITS, int G, bool kX>
-hipError_t launch_d(const RowArgs& a, hipStream_t stream) {
+template <int MODE, int BITS, int G, bool kX, bool kSc>
+hipError_t launch_dd(const RowArgs& a, hipStream_t stream) {
   constexpr int P = Unit<G>::kPos;
   switch (a.d) {
-    case 1024: return launch_typed<MODE, BITS, G, 1024 / P, 1, kX>(a, stream);
-    case 2048: return launch_typed<MODE, BITS, G, 2048 / P, 1, kX>(a, stream);
-    case 3072: if constexpr (3072 % P == 0) return launch_typed<MODE, BITS, G, 3072 / P, 1, kX>(a, stream);
+    case 1024: return launch_typed<MODE, BITS, G, 1024 / P, 1, kX, kSc>(a, stream);
+    case 2048: return launch_typed<MODE, BITS, G, 2048 / P, 1, kX, kSc>(a, stream);
+    case 3072: if constexpr (3072 % P == 0) return launch_typed<MODE, BITS, G, 3072 / P, 1, kX, kSc>(a, stream);
                break;
-    case 4096: return launch_typed<MODE, BITS, G, 4096 / P, 1, kX>(a, stream);
-    case 8192: return launch_typed<MODE, BITS, G, 8192 / P / 4, 4, kX>(a, stream);
-    case 12288: return launch_typed<MODE, BITS, G, 12288 / P / 4, 4, kX>(a, stream);
-    case 16384: return launch_typed<MODE, BITS, G, 16384 / P / 4, 4, kX>(a, stream);
+    case 4096: return launch_typed<MODE, BITS, G, 4096 / P, 1, kX, kSc>(a, stream);
+    case 8192: return launch_typed<MODE, BITS, G, 8192 / P / 4, 4, kX, kSc>(a, stream);
+    case 12288: return launch_typed<MODE, BITS, G, 12288 / P / 4, 4, kX, kSc>(a, stream);
+    case 16384: return launch_typed<MODE, BITS, G, 16384 / P / 4, 4, kX, kSc>(a, stream);
   }
   return hipErrorInvalidValue;
+}
+
+// The scatter form serves the online activation quantizer (the other modes
+// run offline or keep the gather form).
+template <int MODE, int BITS, int G, bool kX>
+hipError_t launch_d(const RowArgs& a, hipStream_t stream) {
+  if constexpr (MODE == kAct) {
+    if (a.scatter_words) return launch_dd<MODE, BITS, G, kX, true>(a, stream);
+  }
+  return launch_dd<MODE, BITS, G, kX, false>(a, stream);
 }
 
 
@@ -466,6 +522,7 @@ void big_kernel(RowArgs a) {
   const floatx4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
 
   for (; row < a.rows; row += gridDim.x) {
+    opaque_words(w);
     float ssx = 0.0f;
 #pragma unroll
     for (int i = 0; i < NU; ++i) {

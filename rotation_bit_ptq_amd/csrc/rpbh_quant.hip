@@ -72,6 +72,10 @@ hipError_t launch_rows(const RowJob& job, hipStream_t stream) {
   if (job.gather && fast == tr_order) a.gather = job.gather;
   const uint32_t* words = job.gather && mfma_words_len(job.d, job.h) > 0
                               ? (const uint32_t*)(job.gather + gather_len(job.d)) : nullptr;
+  // the scatter section serves permuting rotations (an identity permutation
+  // reads the padded row in place, without bank conflicts)
+  const uint32_t* scatter = job.gather && !job.perm_identity && scatter_len(job.d, job.h) > 0
+      ? (const uint32_t*)(job.gather + gather_len(job.d) + mfma_words_len(job.d, job.h)) : nullptr;
   const bool rot_f16 = job.mode == RowMode::kRotate && job.out_dtype == ORBIT_F16;
   // blocks of 512 .. 4096 coordinates on rows of 2048 or 4096 (the full
   // RHT): the h = 128 factor on the matrix cores, the block bits above it
@@ -91,6 +95,7 @@ hipError_t launch_rows(const RowJob& job, hipStream_t stream) {
   if (bf16 && ((quant && m2_takes(job.d, job.h, job.bits, false)) ||
                (rot_f16 && m2_takes(job.d, job.h, 0, true)))) {
     a.mfma_words = words;
+    a.scatter_words = scatter;
     const bool act = job.mode == RowMode::kActQuant;
     if (job.h == 128) {
       if (rot_f16) return launch_m2<kRotF16, 4>(a, 0, stream);
@@ -225,11 +230,41 @@ __global__ __launch_bounds__(256) void mfma_words_kernel(int d, int h, const int
   out[i] = a0 | (s0 << 15) | (a1 << 16) | (s1 << 31);
 }
 
+// The plan's scatter section (h = 128 / 256 packed-code kernels): entry
+// pi(k) holds the byte offset 16 (64 o + l) + 2 j of slot j of lane l in A
+// operand o, the slot whose permuted coordinate is k (the inverse of
+// m2::slot_k), and D_k in bit 15.  A lane that loaded x[i] writes it,
+// sign-flipped, to that offset: the operands then lie in LDS as 16
+// contiguous bytes per lane.
+__global__ __launch_bounds__(256) void scatter_words_kernel(int d, int h, const int32_t* perm,
+                                                            const uint32_t* sign_bits, uint16_t* out) {
+  const int k = blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= d) return;
+  int o, kq, r16, j;
+  if (h == 128) {  // k = 512 o + 128 (r16 / 4) + 32 kq + 4 j + r16 % 4
+    o = k >> 9;
+    kq = (k >> 5) & 3;
+    j = (k >> 2) & 7;
+    r16 = 4 * ((k >> 7) & 3) + (k & 3);
+  } else {         // k = 1024 (o / 2) + 256 (r16 / 4) + 64 kq + 8 j + 4 (o % 2) + r16 % 4
+    o = 2 * (k >> 10) + ((k >> 2) & 1);
+    kq = (k >> 6) & 3;
+    j = (k >> 3) & 7;
+    r16 = 4 * ((k >> 8) & 3) + (k & 3);
+  }
+  const uint32_t off = 16u * (uint32_t)(64 * o + 16 * kq + r16) + 2u * (uint32_t)j;
+  const uint32_t neg = (sign_bits[k >> 5] >> (k & 31)) & 1u;
+  out[perm[k]] = (uint16_t)(off | (neg << 15));
+}
+
 hipError_t launch_gather_plan(int d, int h, const int32_t* perm, const uint32_t* sign_bits,
                               uint16_t* out, hipStream_t stream) {
   if (mfma_words_len(d, h) > 0)
     hipLaunchKernelGGL(mfma_words_kernel, dim3((d / 2 + 255) / 256), dim3(256), 0, stream, d, h, perm,
                        sign_bits, (uint32_t*)(out + gather_len(d)));
+  if (scatter_len(d, h) > 0)
+    hipLaunchKernelGGL(scatter_words_kernel, dim3((d + 255) / 256), dim3(256), 0, stream, d, h, perm,
+                       sign_bits, out + gather_len(d) + mfma_words_len(d, h));
   const dim3 grid(gather_len(d) / 256), block(256);
   if (h == 64) hipLaunchKernelGGL(gather_plan_kernel<2>, grid, block, 0, stream, d, perm, sign_bits, out);
   else if (h == 128) hipLaunchKernelGGL(gather_plan_kernel<3>, grid, block, 0, stream, d, perm, sign_bits, out);

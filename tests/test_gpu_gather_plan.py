@@ -82,16 +82,42 @@ def _words_reference(perm, signs, h):
     return out
 
 
+def _scatter_reference(perm, signs, h):
+    """The documented scatter section (h = 128 / 256 on rows of 1024, 2048,
+    3072, 4096, 8192, 12288 or 16384 coordinates, else empty): entry i is
+    the LDS byte offset 16 (64 o + l) + 2 j of the operand slot (o, l, j)
+    whose permuted coordinate k (the slot order of the offset words) has
+    pi(k) = i, with D_k in bit 15."""
+    d = perm.shape[0]
+    if h not in (128, 256) or d not in (1024, 2048, 3072, 4096, 8192, 12288, 16384):
+        return np.zeros(0, dtype=np.int64)
+    out = np.full(d, -1, dtype=np.int64)
+    for o in range(d // 512):
+        for lane in range(64):
+            kq, r16 = divmod(lane, 16)
+            for j in range(8):
+                if h == 128:
+                    k = 512 * o + 128 * (r16 // 4) + 32 * kq + 4 * j + r16 % 4
+                else:
+                    k = 1024 * (o // 2) + 256 * (r16 // 4) + 64 * kq + 8 * j + 4 * (o % 2) + r16 % 4
+                out[int(perm[k])] = 16 * (64 * o + lane) + 2 * j + (int(signs[k] < 0) << 15)
+    assert (out >= 0).all()
+    return out
+
+
 def _check_plan(rot, perm, signs, h, rounds):
     got = rot.gather.cpu().numpy()
     n = 1024 * rounds
     words = _words_reference(perm, signs, h)
-    assert got.shape == (n + 2 * words.shape[0],)
+    scat = _scatter_reference(perm, signs, h)
+    nw = 2 * words.shape[0]
+    assert got.shape == (n + nw + scat.shape[0],)
     assert np.array_equal(got[:n].view(np.uint16).astype(np.int64), _plan_reference(perm, signs, h, rounds))
-    assert np.array_equal(got[n:].view(np.uint32).astype(np.int64), words)
+    assert np.array_equal(got[n:n + nw].view(np.uint32).astype(np.int64), words)
+    assert np.array_equal(got[n + nw:].view(np.uint16).astype(np.int64), scat)
 
 
-@pytest.mark.parametrize("d,h", [(3072, 128), (1024, 64), (2048, 256), (512, 32), (96, 16),
+@pytest.mark.parametrize("d,h", [(3072, 128), (1024, 64), (2048, 256), (3072, 256), (512, 32), (96, 16),
                                  (4096, 4096), (2048, 512)])
 def test_plan_layout(gpu_lib, d, h):
     perm, signs = synth.rotation_params(d, 7 + d + h)
@@ -163,3 +189,43 @@ def test_weight_rotate_int8_same_with_and_without_plan(gpu_lib, h):
     qa, sa = rbp.int8_pack_weights(a, W)
     qb, sb = rbp.int8_pack_weights(b, W)
     assert torch.equal(qa, qb) and torch.equal(sa.view(torch.int16), sb.view(torch.int16))
+
+
+def test_plan_refuses_a_perm_that_is_not_a_permutation(gpu_lib):
+    """The scatter section has one entry per input coordinate, so the plan
+    builder checks that perm is a permutation before it launches anything."""
+    perm, signs = synth.rotation_params(1024, 5)
+    bad = perm.copy()
+    bad[3] = bad[7]                       # one index twice, one missing
+    with pytest.raises(gpu_lib.OrbitError, match="status 1"):
+        gpu_lib.Rotation(bad, signs, 128)
+    out_of_range = perm.copy()
+    out_of_range[0] = 1024
+    with pytest.raises(gpu_lib.OrbitError, match="status 1"):
+        gpu_lib.Rotation(out_of_range, signs, 128)
+
+
+@pytest.mark.parametrize("d,h,bits", [(3072, 128, 4), (2048, 128, 6), (1024, 256, 2), (3072, 256, 4),
+                                      (4096, 128, 8), (8192, 256, 4), (16384, 128, 4)])
+def test_scatter_and_gather_forms_agree(gpu_lib, d, h, bits):
+    """The activation quantizer's two forms on a permuting rotation: with the
+    plan the lanes scatter the row into operand order, without it they
+    gather their operands; the codes, norms and x' must be bit-identical
+    (the same MFMA operands in the same order), on enough rows that waves
+    loop over several."""
+    rbp = gpu_lib
+    perm, signs = synth.rotation_params(d, d + h + bits)
+    g = np.random.default_rng(d + bits)
+    M = 2100 if d <= 4096 else 700
+    X = to_dev(synth.f32_to_bf16_bits(g.standard_normal((M, d)).astype(np.float32)))
+    cb = rbp.Codebook(d, bits)
+    with_plan = rbp.Rotation(perm, signs, h)
+    without = rbp.Rotation(perm, signs, h, plan=False)
+    i1, s1 = rbp.quant_act(with_plan, cb, X, synth.EPS)
+    i2, s2 = rbp.quant_act(without, cb, X, synth.EPS)
+    i3, s3, x3 = rbp.quant_act(with_plan, cb, X[:300], synth.EPS, debug_xrot=True)
+    i4, s4, x4 = rbp.quant_act(without, cb, X[:300], synth.EPS, debug_xrot=True)
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2) and torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+    assert torch.equal(i3, i4) and torch.equal(x3.view(torch.int32), x4.view(torch.int32))
+    assert torch.equal(i3, i1[:300])

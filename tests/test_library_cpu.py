@@ -159,10 +159,12 @@ def test_status_strings():
 
 
 @pytest.mark.parametrize("d,h,expect", [
-    (3072, 128, 4096 + 3072),    # butterfly section (at least 4 rounds) + matrix-core words
-    (1024, 64, 4096 + 1024),
-    (12288, 256, 12288 + 12288),
-    (16384, 128, 16384 + 16384),
+    (3072, 128, 4096 + 3072 + 3072),   # butterfly section (at least 4 rounds) + matrix-core
+                                       # words + scatter section (h = 128 / 256 packed-code rows)
+    (1024, 64, 4096 + 1024),           # h = 64: no scatter section
+    (12288, 256, 12288 + 12288 + 12288),
+    (16384, 128, 16384 + 16384 + 16384),
+    (5120, 128, 5120 + 5120),          # a row width the packed-code kernel does not take
     (512, 32, 4096),             # h = 32: no matrix-core kernel, no words
     (96, 16, 4096),              # d not a multiple of 512
     (2048, 512, 4096 + 2048),   # blocks of 512 .. 4096: the h = 128 order of words
