@@ -65,6 +65,7 @@ struct RowArgs {
   int perm_identity;       // 1: perm[k] == k (the matrix-core kernels read rows directly)
   const void* in;
   float sqrt_d_over_h;  // sqrt(d / h): u = z * sqrt(d/h) / (s + eps), z = H y unnormalised
+  float sqrt_h_over_d;  // its reciprocal: 1 / alpha = (s + eps) * sqrt(h/d)
   float inv_sqrt_h;
   float inv_h;
   float eps;
@@ -537,6 +538,27 @@ __device__ __forceinline__ float row_alpha(const RowArgs& a, float ss, long long
     return r > 0.0f ? a.sqrt_d_over_h / r : 0.0f;
   } else {
     return 0.0f;
+  }
+}
+
+// As row_alpha, and 1 / alpha for the per-row threshold rewrite: for
+// activations (s + eps) sqrt(h/d), one multiply instead of a division on
+// the row's dependency chain (both round within a few float32 ulps of the
+// exact quotient); for weights 1 / alpha as before (a zero row gives an
+// infinite factor, so its thresholds keep their signs).
+template <int MODE>
+__device__ __forceinline__ float row_alpha_inv(const RowArgs& a, float ss, long long row, int lane,
+                                               float& inv) {
+  if constexpr (MODE == kAct) {
+    const float s = sqrtf(ss);
+    if (lane == 0) a.s_out[row] = s;
+    const float se = s + a.eps;
+    inv = se * a.sqrt_h_over_d;
+    return a.sqrt_d_over_h / se;
+  } else {
+    const float alpha = row_alpha<MODE, true>(a, ss, row, lane);
+    inv = 1.0f / alpha;
+    return alpha;
   }
 }
 

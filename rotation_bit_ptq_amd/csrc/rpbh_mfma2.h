@@ -251,11 +251,26 @@ __device__ __forceinline__ void units(const RowArgs& a, long long row, int u0,
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
         Packed packed = 0;
+        if constexpr (RUN == 4 && BITS == 4) {
+          // a tree of three shift-ors (the compiler's own form of the chain
+          // took four: two shifts, a shift-or and an or3); the empty asm
+          // keeps the pairs from being re-associated
+          uint32_t id[4];
 #pragma unroll
-        for (int c = RUN - 1; c >= 0; --c) {
-          const GridCell& gc = g[(st - 1) & 1][RUN * r + c];
-          const int idx = gc.base + (gc.t < uu[(st - 1) & 1][RUN * r + c] ? 1 : 0);
-          packed = (Packed)(packed << BITS) | (Packed)idx;
+          for (int c = 0; c < 4; ++c) {
+            const GridCell& gc = g[(st - 1) & 1][RUN * r + c];
+            id[c] = (uint32_t)(gc.base + (gc.t < uu[(st - 1) & 1][RUN * r + c] ? 1 : 0));
+          }
+          uint32_t lo = (id[1] << 4) | id[0], hi = (id[3] << 4) | id[2];
+          asm volatile("" : "+v"(lo), "+v"(hi));
+          packed = (hi << 8) | lo;
+        } else {
+#pragma unroll
+          for (int c = RUN - 1; c >= 0; --c) {
+            const GridCell& gc = g[(st - 1) & 1][RUN * r + c];
+            const int idx = gc.base + (gc.t < uu[(st - 1) & 1][RUN * r + c] ? 1 : 0);
+            packed = (Packed)(packed << BITS) | (Packed)idx;
+          }
         }
         uint8_t* out = a.idx_out + (size_t)row * ((size_t)D * BITS / 8) +
                        (size_t)run_pos(st - 1, r) * BITS / 8;
@@ -371,14 +386,23 @@ void kernel(RowArgs a) {
   // a few float32 ulps of a threshold.
   GridCell* const grid = (GridCell*)(smem + kGrid);
   float* const thr = (float*)(smem + kGrid + a.grid_bytes);
+  // grids of at most one cell per thread (the usual case: 32 cells for
+  // 4-bit codes) keep the thread's threshold in a register, so the per-row
+  // rewrite waits on no LDS read
+  const bool thr_in_reg = a.cells <= NT;
+  float thr_r = 0.0f;
   if constexpr (kQuant) {
     build_grid(a, smem + kGrid);
     __syncthreads();
     for (int c = t; c < a.cells; c += NT) thr[c] = grid[c].t;
+    if (thr_in_reg && t < a.cells) thr_r = grid[t].t;
   }
-  auto rescale = [&](float alpha) {
-    const float inv = 1.0f / alpha;
-    for (int c = t; c < a.cells; c += NT) grid[c].t = thr[c] * inv;
+  auto rescale = [&](float inv) {
+    if (thr_in_reg) {
+      if (t < a.cells) grid[t].t = thr_r * inv;
+    } else {
+      for (int c = t; c < a.cells; c += NT) grid[c].t = thr[c] * inv;
+    }
   };
 
   for (; row < a.rows; row += gridDim.x) {
@@ -400,8 +424,9 @@ void kernel(RowArgs a) {
     float alpha = 0.0f;
     if constexpr (W == 1) {
       if constexpr (kQuant) {
-        alpha = row_alpha<MODE, true>(a, wave_sum(ssx), row, lane);
-        rescale(alpha);
+        float inv;
+        alpha = row_alpha_inv<MODE>(a, wave_sum(ssx), row, lane, inv);
+        rescale(inv);
       }
       __syncthreads();  // the row and the row's thresholds are in LDS
     } else {
@@ -411,8 +436,9 @@ void kernel(RowArgs a) {
       }
       __syncthreads();  // the row and the wave sums are in LDS
       if constexpr (kQuant) {
-        alpha = row_alpha<MODE, true>(a, (red[0] + red[1]) + (red[2] + red[3]), row, t);
-        rescale(alpha);
+        float inv;
+        alpha = row_alpha_inv<MODE>(a, (red[0] + red[1]) + (red[2] + red[3]), row, t, inv);
+        rescale(inv);
         __syncthreads();  // the row's thresholds are in LDS
       }
     }

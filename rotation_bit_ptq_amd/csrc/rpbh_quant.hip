@@ -24,6 +24,7 @@ hipError_t launch_rows(const RowJob& job, hipStream_t stream) {
   a.perm_identity = job.perm_identity ? 1 : 0;
   a.in = job.in;
   a.sqrt_d_over_h = (float)sqrt((double)job.d / job.h);
+  a.sqrt_h_over_d = (float)sqrt((double)job.h / job.d);
   a.inv_sqrt_h = (float)(1.0 / sqrt((double)job.h));
   a.inv_h = (float)(1.0 / job.h);
   a.eps = job.eps;
