@@ -24,11 +24,18 @@
 // positions 4 j' + e (h = 128) or 8 j' + 4 m + e (h = 256), j' = r16 or
 // r16 + 16, i.e. 4 or 8 consecutive positions.
 //
-// Per row: the row lands once in LDS (at address 0, with a 16-byte pad
-// after every 64 coordinates up to 12288 coordinates, so that the strided
-// reads of an identity permutation spread over the banks), and each lane
-// gathers its operand pairs with two 16-bit reads from the plan's offset
-// words, which also carry the sign flips D (XOR into bits 15 and 31).
+// Per row, one of two forms brings each lane's A operands into LDS order:
+//   * scatter (activations on a permuting rotation with a plan): each lane
+//     writes the bf16 values it loaded, sign-flipped by D, straight to the
+//     operand slots the plan's scatter section names, so every operand is
+//     16 contiguous bytes and one 16-byte read;
+//   * gather (everything else): the row lands once in LDS (at address 0,
+//     with a 16-byte pad after every 64 coordinates up to 12288
+//     coordinates, so that the strided reads of an identity permutation
+//     spread over the banks), and each lane gathers its operand pairs with
+//     two 16-bit reads from the plan's offset words (or words built from pi
+//     and the signs), which also carry the sign flips D (XOR into bits 15
+//     and 31).
 #pragma once
 
 #include <type_traits>
