@@ -39,6 +39,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settle-ms", type=float, default=60.0,
+                    help="run the step loop untimed for this much device time before the "
+                         "warm-up steps, so that the timed steps see the clock the matrix "
+                         "cores hold under sustained load (0: no settling)")
     ap.add_argument("--traffic", default=os.path.join(HERE, "profiles", "traffic.json"),
                     help="per-launch HBM bytes measured with rocprofv3 counters")
     ap.add_argument("--only", choices=["quant", "gemm", "copy", "mfma", "video_quant",
@@ -591,6 +595,44 @@ def main():
                           "copy_bytes": COPY_BYTES if args.only == "copy" else None}), flush=True)
         return
 
+    # Settling.  From a lightly loaded device the first milliseconds of the
+    # step loop run at a boosted clock, the power controller then pulls the
+    # clock below its sustained level for several milliseconds (the GEMM
+    # goes from ~70 us to ~86 us and back), and the step time settles after
+    # ~50 ms.  A serving loop runs at the settled rate, so the step loop runs
+    # untimed for settle_ms of device time first, in chunks of ten steps with
+    # an event after each; the first and last chunks are reported.
+    settle = None
+    if args.settle_ms > 0:
+        per, i = 10, 0
+        chunks = []
+
+        def enqueue_chunk():
+            nonlocal i
+            for _ in range(per):
+                quant(pool[i % pool_n])
+                gemm()
+                i += 1
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(stream)
+            return e
+
+        ev = [torch.cuda.Event(enable_timing=True)]
+        ev[0].record(stream)
+        ev.append(enqueue_chunk())
+        done_ms = 0.0
+        while done_ms < args.settle_ms:
+            ev.append(enqueue_chunk())   # the device stays busy while the host waits
+            ev[-2].synchronize()
+            ms = ev[-3].elapsed_time(ev[-2])
+            chunks.append(ms * 1e3 / per)
+            done_ms += ms
+        # the first chunk also holds the kernels' first launches in the
+        # process; the next ones show the clock's transient
+        settle = {"device_ms": round(done_ms, 2), "steps": i, "chunk_steps": per,
+                  "us_per_step_chunks_2_to_9": [round(c, 1) for c in chunks[1:9]],
+                  "us_per_step_last_chunk": round(chunks[-1], 2)}
+
     for i in range(args.warmup):
         quant(pool[i % pool_n])
         gemm()
@@ -693,6 +735,7 @@ def main():
         "quant_warm_gbps": round(quant_bytes / warm["mean_us"] / 1e3, 1),
         "gemm_launch": gst,
         "measured_peaks": peaks,
+        "settle": settle,
         "step_device_ms": round(device_ms_per_step, 5),
         "step_host_enqueue_ms": round(enqueue / args.steps * 1e3, 5),
         "step_gemm_us": round(tg_step.mean() * 1e6, 2),
