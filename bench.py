@@ -621,7 +621,7 @@ def main():
         ev[0].record(stream)
         ev.append(enqueue_chunk())
         done_ms = 0.0
-        while done_ms < args.settle_ms:
+        while done_ms < args.settle_ms and len(chunks) < 100000:
             ev.append(enqueue_chunk())   # the device stays busy while the host waits
             ev[-2].synchronize()
             ms = ev[-3].elapsed_time(ev[-2])
